@@ -1,0 +1,354 @@
+/*
+ * vq_oracle.c -- plain CPU oracle for the vector-quantized MoE expert matmul.
+ *
+ * TEST INFRASTRUCTURE ONLY (see vq_oracle.h): used by the test suite, the
+ * smoke check and the benchmark's CPU-baseline leg, never by the product path.
+ *
+ * Written for clarity, not speed: codes are unpacked one bit at a time,
+ * weights are decoded to a dense fp32 matrix, and every dot product is a
+ * straight fp64 loop with the column index ascending.  OpenMP only splits
+ * independent output rows across threads; it does not change any sum.
+ */
+#include "vq_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------------- */
+/* Number formats                                                          */
+/* ---------------------------------------------------------------------- */
+
+/* IEEE 754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+   bits.  Normal: (-1)^s * 2^(e-15) * (1 + f/1024).  Subnormal (e == 0):
+   (-1)^s * 2^-14 * (f/1024).  e == 31: infinity (f == 0) or NaN.
+   The model cards store codebooks and scales in this format ("fp16"). */
+double vqo_half_to_double(uint16_t h)
+{
+    int s = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);               /* f/1024 * 2^-14 */
+    else if (e == 31)
+        v = (f == 0) ? INFINITY : NAN;
+    else
+        v = ldexp((double)(1024 + f), e - 25);   /* (1+f/1024) * 2^(e-15) */
+    return s ? -v : v;
+}
+
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits.
+   Normal: (-1)^s * 2^(e-127) * (1 + f/128).  Subnormal: (-1)^s * 2^-126 *
+   (f/128).  e == 255: infinity or NaN.  Activations arrive in this format
+   ("bf16 I/O" on the Qwen3.8-Flash-Next-VQ-4.4bpw card, changelog 2026-09-17). */
+double vqo_bf16_to_double(uint16_t h)
+{
+    int s = (h >> 15) & 1;
+    int e = (h >> 7) & 0xff;
+    int f = h & 0x7f;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -133);              /* f/128 * 2^-126 */
+    else if (e == 255)
+        v = (f == 0) ? INFINITY : NAN;
+    else
+        v = ldexp((double)(128 + f), e - 134);   /* (1+f/128) * 2^(e-127) */
+    return s ? -v : v;
+}
+
+static double x_value(const void *x, int32_t dtype, int64_t i)
+{
+    if (dtype == VQO_X_F32) {
+        float f;
+        memcpy(&f, (const char *)x + 4 * i, 4);
+        return (double)f;
+    }
+    if (dtype == VQO_X_BF16)
+        return vqo_bf16_to_double(((const uint16_t *)x)[i]);
+    return ((const double *)x)[i];
+}
+
+/* ---------------------------------------------------------------------- */
+/* Step 1: the packed code stream                                          */
+/* ---------------------------------------------------------------------- */
+
+/* Model card "Qwen3.5-397B-A17B-VQ-2.6bpw", section "Sub-byte bit-packing":
+   codes are packed into uint32 words, row-local, in 32-code blocks.  32 codes
+   of b bits fill exactly b words, so a row of n_sub = cols/d codes takes
+   ceil(n_sub/32) blocks = ceil(n_sub/32) * b words (the tail of the last
+   block is padding). */
+int64_t vqo_words_per_row(int32_t cols, int32_t d, int32_t bits)
+{
+    int64_t n_sub = cols / d;
+    return ((n_sub + 31) / 32) * (int64_t)bits;
+}
+
+/* Code j = stream bits [j*b, j*b + b), least significant bit first; stream
+   bit q is bit (q mod 32) of word q / 32.  Assembled one bit at a time. */
+uint32_t vqo_code(const uint32_t *row_words, int32_t bits, int64_t j)
+{
+    uint32_t code = 0;
+    for (int32_t i = 0; i < bits; ++i) {
+        int64_t q = j * (int64_t)bits + i;
+        uint32_t bit = (row_words[q / 32] >> (q % 32)) & 1u;
+        code |= bit << i;
+    }
+    return code;
+}
+
+void vqo_unpack_row(const uint32_t *row_words, int32_t bits, int64_t n, uint32_t *out)
+{
+    for (int64_t j = 0; j < n; ++j)
+        out[j] = vqo_code(row_words, bits, j);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Descriptor checks                                                       */
+/* ---------------------------------------------------------------------- */
+
+static int64_t stored_row(const vqo_tensor *T, int32_t e, int32_t r)
+{
+    if (T->row_map == NULL)
+        return (int64_t)e * T->rows + r;
+    return T->row_map[(int64_t)e * T->rows + r];
+}
+
+int vqo_check(const vqo_tensor *T)
+{
+    if (!T || T->rows < 0 || T->cols < 0 || T->n_experts < 1)
+        return VQO_EBADARG;
+    if (T->d != 1 && T->d != 2 && T->d != 4 && T->d != 8)
+        return VQO_EBADARG;
+    if (T->cols % 64 != 0 || T->bits < 0 || T->bits > 16)
+        return VQO_EBADARG;
+    if (T->K < 1 || (int64_t)T->K > ((int64_t)1 << T->bits))
+        return VQO_EBADARG;
+    if (T->row_map == NULL && T->n_stored != (int64_t)T->n_experts * T->rows)
+        return VQO_EMAP;
+    /* Every stored row referenced at most once, every index in range. */
+    if (T->row_map != NULL) {
+        char *seen = (char *)calloc((size_t)(T->n_stored > 0 ? T->n_stored : 1), 1);
+        if (!seen)
+            return VQO_ENOMEM;
+        for (int64_t i = 0; i < (int64_t)T->n_experts * T->rows; ++i) {
+            int32_t s = T->row_map[i];
+            if (s < -1 || s >= T->n_stored || (s >= 0 && seen[s])) {
+                free(seen);
+                return VQO_EMAP;
+            }
+            if (s >= 0)
+                seen[s] = 1;
+        }
+        free(seen);
+    }
+    int64_t wpr = vqo_words_per_row(T->cols, T->d, T->bits);
+    int64_t n_sub = T->cols / T->d;
+    for (int64_t s = 0; s < T->n_stored; ++s)
+        for (int64_t j = 0; j < n_sub; ++j)
+            if (vqo_code(T->codes + s * wpr, T->bits, j) >= (uint32_t)T->K)
+                return VQO_ECODE;
+    return VQO_OK;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Step 2: decode to dense weights                                         */
+/* ---------------------------------------------------------------------- */
+
+/* Model card "Qwen3.5-397B-A17B-VQ-2.6bpw", section "Methodology": each
+   d-weight subvector stores one index into a per-tensor fp16 codebook, with
+   an fp16 scale per (row, 64 weights).  Subvector j of row r covers columns
+   [j*d, j*d + d); its scale is the one of group (j*d)/64.  The product of
+   two fp16 numbers has at most 22 significant bits and an exponent well
+   inside fp32's range, so computing it in double and storing it as float is
+   exact.  Skip-zero ("Qwen3.5-397B-A17B-VQ-2.4bpw: Model Card", changelog
+   2026-10-01): a dead row has no codes or scales and is exactly zero. */
+int vqo_decode(const vqo_tensor *T, int32_t e, float *W)
+{
+    if (!T || e < 0 || e >= T->n_experts || !W)
+        return VQO_EBADARG;
+    const int64_t wpr = vqo_words_per_row(T->cols, T->d, T->bits);
+    const int64_t groups = T->cols / 64;
+    const int64_t n_sub = T->cols / T->d;
+    int err = VQO_OK;
+
+#pragma omp parallel for schedule(static)
+    for (int32_t r = 0; r < T->rows; ++r) {
+        float *wr = W + (int64_t)r * T->cols;
+        int64_t s = stored_row(T, e, r);
+        if (s < 0) {
+            for (int32_t c = 0; c < T->cols; ++c)
+                wr[c] = 0.0f;
+            continue;
+        }
+        if (s >= T->n_stored) {
+#pragma omp atomic write
+            err = VQO_EMAP;
+            continue;
+        }
+        const uint32_t *words = T->codes + s * wpr;
+        const uint16_t *srow = T->scales + s * groups;
+        for (int64_t j = 0; j < n_sub; ++j) {
+            uint32_t code = vqo_code(words, T->bits, j);
+            if (code >= (uint32_t)T->K) {
+#pragma omp atomic write
+                err = VQO_ECODE;
+                code = 0;
+            }
+            double scale = vqo_half_to_double(srow[(j * T->d) / 64]);
+            for (int32_t t = 0; t < T->d; ++t) {
+                double c = vqo_half_to_double(T->codebook[(int64_t)code * T->d + t]);
+                wr[j * T->d + t] = (float)(scale * c);
+            }
+        }
+    }
+    return err;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Step 3: the matmul                                                      */
+/* ---------------------------------------------------------------------- */
+
+/* y = W x with W [out][in] (the subvector runs along the input dimension of
+   one output row, as in "an fp16 scale per (row, 64 weights)").  Every sum
+   is an fp64 loop over ascending columns. */
+static void matvec_f64(const float *W, int32_t rows, int32_t cols,
+                       const double *x, double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int32_t r = 0; r < rows; ++r) {
+        const float *wr = W + (int64_t)r * cols;
+        double acc = 0.0;
+        for (int32_t c = 0; c < cols; ++c)
+            acc += (double)wr[c] * x[c];
+        y[r] = acc;
+    }
+}
+
+int vqo_linear(const vqo_tensor *T, int32_t e, int32_t n_tok,
+               const void *x, int32_t x_dtype, double *y)
+{
+    if (!T || n_tok < 0 || (n_tok > 0 && (!x || !y)))
+        return VQO_EBADARG;
+    if (x_dtype != VQO_X_F32 && x_dtype != VQO_X_BF16 && x_dtype != VQO_X_F64)
+        return VQO_EBADARG;
+    float *W = (float *)malloc(sizeof(float) * (size_t)T->rows * (size_t)T->cols + 1);
+    double *xv = (double *)malloc(sizeof(double) * (size_t)T->cols + 1);
+    if (!W || !xv) {
+        free(W);
+        free(xv);
+        return VQO_ENOMEM;
+    }
+    int err = vqo_decode(T, e, W);
+    for (int32_t n = 0; n < n_tok && err == VQO_OK; ++n) {
+        for (int32_t c = 0; c < T->cols; ++c)
+            xv[c] = x_value(x, x_dtype, (int64_t)n * T->cols + c);
+        matvec_f64(W, T->rows, T->cols, xv, y + (int64_t)n * T->rows);
+    }
+    free(W);
+    free(xv);
+    return err;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Step 4: the routed SwiGLU expert FFN                                    */
+/* ---------------------------------------------------------------------- */
+
+/* SwiGLU: h = silu(gate) * up with silu(z) = z * sigmoid(z) = z / (1 + e^-z). */
+double vqo_swiglu(double g, double u)
+{
+    return g / (1.0 + exp(-g)) * u;
+}
+
+/* Each token t is routed to top_k experts ids[t][0..k) with gate weights
+   w[t][0..k) (the Qwen3.8-Flash-Next card: 10 of 512 experts; the gemma-4
+   card: 128 experts, top-8).  Expert e applies gate, up and down projections
+   of its own; the token's output is the gate-weighted sum over its slots,
+   taken in slot order. */
+int vqo_moe_ffn(const vqo_tensor *gate, const vqo_tensor *up, const vqo_tensor *down,
+                int32_t n_tok, int32_t top_k, const void *x, int32_t x_dtype,
+                const int32_t *ids, const float *w,
+                int32_t n_sel, const int32_t *tokens, double *y)
+{
+    if (!gate || !up || !down || n_tok < 0 || top_k < 1 || n_sel < 0)
+        return VQO_EBADARG;
+    if (n_sel > 0 && (!x || !ids || !w || !tokens || !y))
+        return VQO_EBADARG;
+    if (x_dtype != VQO_X_F32 && x_dtype != VQO_X_BF16 && x_dtype != VQO_X_F64)
+        return VQO_EBADARG;
+    const int32_t hidden = gate->cols, inter = gate->rows;
+    const int32_t E = gate->n_experts;
+    if (up->cols != hidden || up->rows != inter || down->cols != inter ||
+        down->rows != hidden || up->n_experts != E || down->n_experts != E)
+        return VQO_EBADARG;
+    for (int32_t i = 0; i < n_sel; ++i)
+        if (tokens[i] < 0 || tokens[i] >= n_tok)
+            return VQO_EBADARG;
+    for (int32_t i = 0; i < n_sel; ++i)
+        for (int32_t s = 0; s < top_k; ++s) {
+            int32_t e = ids[(int64_t)tokens[i] * top_k + s];
+            if (e < 0 || e >= E)
+                return VQO_EBADARG;
+        }
+
+    const size_t nz = (size_t)n_sel * top_k * hidden;
+    double *z = (double *)calloc(nz + 1, sizeof(double));
+    float *Wg = (float *)malloc(sizeof(float) * (size_t)inter * hidden + 1);
+    float *Wu = (float *)malloc(sizeof(float) * (size_t)inter * hidden + 1);
+    float *Wd = (float *)malloc(sizeof(float) * (size_t)hidden * inter + 1);
+    double *xv = (double *)malloc(sizeof(double) * (size_t)hidden + 1);
+    double *g = (double *)malloc(sizeof(double) * (size_t)inter + 1);
+    double *u = (double *)malloc(sizeof(double) * (size_t)inter + 1);
+    double *h = (double *)malloc(sizeof(double) * (size_t)inter + 1);
+    int err = (z && Wg && Wu && Wd && xv && g && u && h) ? VQO_OK : VQO_ENOMEM;
+
+    /* Decode each expert once, then apply it to every selected (token, slot)
+       routed to it; z[i][s] holds that slot's down-projection output. */
+    for (int32_t e = 0; e < E && err == VQO_OK; ++e) {
+        int used = 0;
+        for (int32_t i = 0; i < n_sel && !used; ++i)
+            for (int32_t s = 0; s < top_k; ++s)
+                if (ids[(int64_t)tokens[i] * top_k + s] == e)
+                    used = 1;
+        if (!used)
+            continue;
+        err = vqo_decode(gate, e, Wg);
+        if (err == VQO_OK)
+            err = vqo_decode(up, e, Wu);
+        if (err == VQO_OK)
+            err = vqo_decode(down, e, Wd);
+        for (int32_t i = 0; i < n_sel && err == VQO_OK; ++i) {
+            int32_t t = tokens[i];
+            for (int32_t s = 0; s < top_k; ++s) {
+                if (ids[(int64_t)t * top_k + s] != e)
+                    continue;
+                for (int32_t c = 0; c < hidden; ++c)
+                    xv[c] = x_value(x, x_dtype, (int64_t)t * hidden + c);
+                matvec_f64(Wg, inter, hidden, xv, g);
+                matvec_f64(Wu, inter, hidden, xv, u);
+                for (int32_t r = 0; r < inter; ++r)
+                    h[r] = vqo_swiglu(g[r], u[r]);
+                matvec_f64(Wd, hidden, inter, h, z + ((size_t)i * top_k + s) * hidden);
+            }
+        }
+    }
+    /* y[t] = sum over slots, in slot order, of w[t][s] * z[t][s]. */
+    for (int32_t i = 0; i < n_sel && err == VQO_OK; ++i) {
+        int32_t t = tokens[i];
+        for (int32_t c = 0; c < hidden; ++c) {
+            double acc = 0.0;
+            for (int32_t s = 0; s < top_k; ++s)
+                acc += (double)w[(int64_t)t * top_k + s] * z[((size_t)i * top_k + s) * hidden + c];
+            y[(int64_t)i * hidden + c] = acc;
+        }
+    }
+    free(z);
+    free(Wg);
+    free(Wu);
+    free(Wd);
+    free(xv);
+    free(g);
+    free(u);
+    free(h);
+    return err;
+}

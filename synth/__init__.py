@@ -1,0 +1,263 @@
+"""Seeded synthetic inputs for the VQ MoE expert matmul.
+
+Both the oracle-based tests and the GPU path draw their inputs from here; this
+module holds none of the method's arithmetic (no unpacking, no decoding, no
+matmul).  It only draws random numbers and writes them in the storage format:
+
+* codebook: fp16 entries ~ N(0, 1), shape [K, d];
+* scales: fp16 ~ U(0.01, 0.05), one per (stored row, 64-column group);
+* codes: uniform on [0, K), written LSB-first into row-local uint32 streams,
+  each row padded to whole 32-code blocks (padding bits are zero).  When
+  K == 2**bits a uniform code is a uniform b-bit field, so the stream is drawn
+  directly as random words and only the padding is cleared;
+* skip-zero: a fixed number of dead rows per (expert, projection), chosen
+  uniformly without replacement; dead rows have no codes or scales and the
+  row map sends them to -1;
+* activations ~ N(0, 1), kept as float32 or rounded to bf16;
+* routes: expert ids uniform without replacement per token, gate weights the
+  softmax of top_k N(0, 1) logits.
+
+The model cards measure on real checkpoints (Qwen3.5-397B-A17B, Qwen3.8-Flash-
+Next, gemma-4-26b-a4b-it, GLM-5.3-Flash); these seeded layers stand in for
+them with the cards' geometries, expert counts and skip-zero fraction.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+
+@dataclass
+class VQTensorHost:
+    """One VQ linear tensor stacked over experts, in host memory."""
+
+    rows: int
+    cols: int
+    d: int
+    bits: int
+    K: int
+    n_experts: int
+    codebook: np.ndarray            # uint16 fp16 bits [K, d]
+    codes: np.ndarray               # uint32 [n_stored, wpr]
+    scales: np.ndarray              # uint16 fp16 bits [n_stored, cols // 64]
+    row_map: Optional[np.ndarray]   # int32 [n_experts * rows], -1 = dead; None = dense
+    raw_codes: Optional[np.ndarray] = None  # int codes [n_stored, n_sub] when kept
+
+    @property
+    def n_stored(self) -> int:
+        return int(self.scales.shape[0])
+
+    @property
+    def n_sub(self) -> int:
+        return self.cols // self.d
+
+    @property
+    def wpr(self) -> int:
+        return words_per_row(self.cols, self.d, self.bits)
+
+    @property
+    def groups(self) -> int:
+        return self.cols // 64
+
+    def stored_bytes(self) -> int:
+        """Bytes of codes + scales + row map as stored."""
+        n = self.codes.nbytes + self.scales.nbytes
+        if self.row_map is not None:
+            n += self.row_map.nbytes
+        return n
+
+    def expert_stored_rows(self, e: int) -> int:
+        if self.row_map is None:
+            return self.rows
+        return int((self.row_map[e * self.rows:(e + 1) * self.rows] >= 0).sum())
+
+
+def words_per_row(cols: int, d: int, bits: int) -> int:
+    """Row-local 32-code blocks of b words each."""
+    n_sub = cols // d
+    return ((n_sub + 31) // 32) * bits
+
+
+def rng_for(seed: int, *stream: int) -> np.random.Generator:
+    """Independent PCG64 stream per (seed, stream ids)."""
+    return np.random.default_rng(np.random.SeedSequence([int(seed), *[int(s) for s in stream]]))
+
+
+def to_half_bits(a: np.ndarray) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round to nearest, ties to even)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def pack_codes(codes: np.ndarray, bits: int) -> np.ndarray:
+    """Write integer codes [n_rows, n_sub] as LSB-first row streams of uint32
+    words, each row padded with zero bits to whole 32-code blocks."""
+    codes = np.asarray(codes, dtype=np.uint32)
+    n_rows, n_sub = codes.shape
+    wpr = ((n_sub + 31) // 32) * bits
+    if bits == 0 or n_rows == 0:
+        return np.zeros((n_rows, wpr), dtype=np.uint32)
+    shifts = np.arange(bits, dtype=np.uint32)
+    stream = ((codes[:, :, None] >> shifts) & 1).astype(np.uint8).reshape(n_rows, n_sub * bits)
+    padded = np.zeros((n_rows, wpr * 32), dtype=np.uint8)
+    padded[:, : n_sub * bits] = stream
+    packed = np.packbits(padded, axis=1, bitorder="little")
+    return np.ascontiguousarray(packed).view("<u4").astype(np.uint32).reshape(n_rows, wpr)
+
+
+def _padding_mask(n_sub: int, bits: int) -> Optional[np.ndarray]:
+    """uint32 mask per word of a row: 1 where the bit belongs to a real code."""
+    wpr = ((n_sub + 31) // 32) * bits
+    used = n_sub * bits
+    if used == wpr * 32:
+        return None
+    mask = np.zeros(wpr, dtype=np.uint64)
+    for w in range(wpr):
+        lo, hi = 32 * w, 32 * w + 32
+        n = max(0, min(hi, used) - lo)
+        mask[w] = (1 << n) - 1
+    return mask.astype(np.uint32)
+
+
+def make_tensor(seed: int, stream: int, *, rows: int, cols: int, d: int, bits: int,
+                K: Optional[int] = None, n_experts: int = 1, dead_rows: int = 0,
+                keep_codes: bool = False) -> VQTensorHost:
+    """A seeded VQ tensor.  ``dead_rows`` rows of every expert are dead
+    (skip-zero).  ``keep_codes`` also returns the integer codes."""
+    K = (1 << bits) if K is None else K
+    if cols % 64 or cols % d:
+        raise ValueError("cols must be a multiple of 64 and of d")
+    if not 1 <= K <= (1 << bits):
+        raise ValueError("need 1 <= K <= 2**bits")
+    if not 0 <= dead_rows <= rows:
+        raise ValueError("dead_rows out of range")
+    g_cb, g_sc, g_code, g_dead = (rng_for(seed, stream, i) for i in range(4))
+    codebook = to_half_bits(g_cb.standard_normal((K, d)))
+
+    row_map = None
+    n_stored = n_experts * rows
+    if dead_rows:
+        row_map = np.full(n_experts * rows, -1, dtype=np.int32)
+        nxt = 0
+        for e in range(n_experts):
+            dead = g_dead.choice(rows, size=dead_rows, replace=False)
+            live = np.ones(rows, dtype=bool)
+            live[dead] = False
+            idx = np.nonzero(live)[0]
+            row_map[e * rows + idx] = np.arange(nxt, nxt + len(idx), dtype=np.int32)
+            nxt += len(idx)
+        n_stored = nxt
+
+    scales = to_half_bits(g_sc.uniform(0.01, 0.05, size=(n_stored, cols // 64)))
+    n_sub = cols // d
+    wpr = words_per_row(cols, d, bits)
+    raw = None
+    if K == (1 << bits) and bits > 0 and not keep_codes:
+        codes = g_code.integers(0, 1 << 32, size=(n_stored, wpr), dtype=np.uint32)
+        mask = _padding_mask(n_sub, bits)
+        if mask is not None:
+            codes &= mask[None, :]
+    else:
+        raw = g_code.integers(0, K, size=(n_stored, n_sub), dtype=np.uint32)
+        codes = pack_codes(raw, bits)
+    return VQTensorHost(rows, cols, d, bits, K, n_experts, codebook,
+                        np.ascontiguousarray(codes), scales, row_map, raw)
+
+
+def make_x(seed: int, stream: int, n_tok: int, cols: int, dtype: str = "bf16") -> np.ndarray:
+    """Activations ~ N(0, 1): float32 values or bf16 bit patterns (uint16)."""
+    x = rng_for(seed, stream).standard_normal((n_tok, cols)).astype(np.float32)
+    if dtype == "f32":
+        return x
+    if dtype == "bf16":
+        return to_bf16_bits(x)
+    raise ValueError(dtype)
+
+
+def make_routes(seed: int, stream: int, n_tok: int, n_experts: int, top_k: int):
+    """Expert ids uniform without replacement per token, gate weights the
+    softmax of top_k N(0, 1) logits (float32)."""
+    g = rng_for(seed, stream)
+    keys = g.random((n_tok, n_experts))
+    ids = np.argsort(keys, axis=1)[:, :top_k].astype(np.int32)
+    logits = g.standard_normal((n_tok, top_k))
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    w = (p / p.sum(axis=1, keepdims=True)).astype(np.float32)
+    return np.ascontiguousarray(ids), np.ascontiguousarray(w)
+
+
+# --------------------------------------------------------------------------
+# The workloads: shapes and geometries of the model cards' MoE layers.
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class MoEWorkload:
+    name: str
+    n_experts: int
+    top_k: int
+    hidden: int
+    inter: int
+    d: int
+    bits: int
+    n_tok: int
+    dead_frac: float = 0.0
+    seed: int = 1234
+
+    def dead_rows(self, rows: int) -> int:
+        return int(round(self.dead_frac * rows))
+
+
+WORKLOADS = {
+    # 128 experts, top-8 (the gemma-4 card's routing), d=4/K=512 9-bit
+    # (the Qwen3.5-397B 2.6bpw and GLM-5.3 base geometry), one token.
+    "moe_decode_e128_h2048_i768_d4k512_b1": MoEWorkload(
+        "moe_decode_e128_h2048_i768_d4k512_b1", 128, 8, 2048, 768, 4, 9, 1, seed=1235),
+    # 10 of 512 experts (the Qwen3.8-Flash-Next card), d=2/K=256 8-bit.
+    "moe_decode_e512_h4096_i1024_d2k256_b1": MoEWorkload(
+        "moe_decode_e512_h4096_i1024_d2k256_b1", 512, 10, 4096, 1024, 2, 8, 1, seed=1236),
+    "moe_decode_e512_h4096_i1024_d2k256_b8": MoEWorkload(
+        "moe_decode_e512_h4096_i1024_d2k256_b8", 512, 10, 4096, 1024, 2, 8, 8, seed=1236),
+    # Its promoted layers: d=2/K=1024, 10-bit packed.
+    "moe_decode_e512_h4096_i1024_d2k1024_b1": MoEWorkload(
+        "moe_decode_e512_h4096_i1024_d2k1024_b1", 512, 10, 4096, 1024, 2, 10, 1, seed=1237),
+    "moe_decode_e512_h4096_i1024_d2k1024_b8": MoEWorkload(
+        "moe_decode_e512_h4096_i1024_d2k1024_b8", 512, 10, 4096, 1024, 2, 10, 8, seed=1237),
+    # Prefill: 2048 tokens, 128 experts top-8, d=4/K=2048 11-bit.
+    "moe_prefill_e128_h2816_i704_d4k2048_t2048": MoEWorkload(
+        "moe_prefill_e128_h2816_i704_d4k2048_t2048", 128, 8, 2816, 704, 4, 11, 2048, seed=1238),
+    # Prefill: 4096 tokens, 512 experts top-10, d=2/K=256, 12.43 % dead groups.
+    "moe_prefill_e512_h4096_i1024_d2k256_t4096_sz": MoEWorkload(
+        "moe_prefill_e512_h4096_i1024_d2k256_t4096_sz", 512, 10, 4096, 1024, 2, 8, 4096,
+        dead_frac=0.1243, seed=1239),
+}
+
+# The single-linear case: weight 256x512 at d=2/K=256, fp32 activations, 1 token.
+LINEAR_256x512 = dict(rows=256, cols=512, d=2, bits=8, n_experts=1, seed=1233)
+
+
+def make_moe_layer(wl: MoEWorkload, layer: int = 0, n_experts: Optional[int] = None):
+    """gate, up, down tensors of one MoE layer (one codebook per projection,
+    shared by the layer's experts)."""
+    E = wl.n_experts if n_experts is None else n_experts
+    gate = make_tensor(wl.seed, 100 * layer + 1, rows=wl.inter, cols=wl.hidden, d=wl.d,
+                       bits=wl.bits, n_experts=E, dead_rows=wl.dead_rows(wl.inter))
+    up = make_tensor(wl.seed, 100 * layer + 2, rows=wl.inter, cols=wl.hidden, d=wl.d,
+                     bits=wl.bits, n_experts=E, dead_rows=wl.dead_rows(wl.inter))
+    down = make_tensor(wl.seed, 100 * layer + 3, rows=wl.hidden, cols=wl.inter, d=wl.d,
+                       bits=wl.bits, n_experts=E, dead_rows=wl.dead_rows(wl.hidden))
+    return gate, up, down
+
+
+def make_moe_inputs(wl: MoEWorkload, step: int = 0, n_experts: Optional[int] = None):
+    """Activations (bf16 bit patterns) and routes for one batch."""
+    E = wl.n_experts if n_experts is None else n_experts
+    x = make_x(wl.seed, 10_000 + step, wl.n_tok, wl.hidden, "bf16")
+    ids, w = make_routes(wl.seed, 20_000 + step, wl.n_tok, E, wl.top_k)
+    return x, ids, w

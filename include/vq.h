@@ -1,0 +1,151 @@
+/*
+ * vq.h -- C ABI of the vector-quantized MoE expert matmul for MI355X (gfx950).
+ *
+ * The weight format is the one described on the VQ model cards:
+ *   - "Qwen3.5-397B-A17B-VQ-2.6bpw", section "Methodology": each d-weight
+ *     subvector of a row stores one b-bit index into a per-tensor fp16
+ *     codebook of K d-vectors, with an fp16 scale per (row, 64 weights);
+ *     section "Sub-byte bit-packing": codes are packed into uint32 words,
+ *     row-local, in 32-code blocks.
+ *   - "GLM-5.3-Flash-VQ-2.7bpw", section "Methodology": 9-bit codes at
+ *     K=512 and 11-bit codes at K=2048, sub-byte packed into uint32 words.
+ *   - "Qwen3.8-Flash-Next-VQ-4.4bpw": d=2/K=256 experts with d=2/K=1024
+ *     (10-bit packed) layers.
+ *   - "Qwen3.5-397B-A17B-VQ-2.4bpw: Model Card", changelog 2026-10-01
+ *     ("vq-skipzero"): dead output rows have no codes or scales and output
+ *     exact zeros.
+ *
+ * Layout of one tensor (one projection of one MoE layer, all experts):
+ *   logical weight of expert e:  W_e[rows][cols]  (out x in), y = W_e x
+ *   n_sub  = cols / d            codes per row
+ *   wpr    = ceil(n_sub/32)*bits uint32 words per stored row
+ *   code j of a stored row = stream bits [j*bits, j*bits+bits), where stream
+ *          bit q is bit (q mod 32) of word q/32 of that row (LSB first); the
+ *          tail of the last 32-code block is zero padding
+ *   W_e[r][j*d+t] = scale[s][(j*d)/64] * codebook[code_j][t],
+ *          s = the stored row of logical row r of expert e
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers; descriptors are host structs
+ *     read during the call and not retained.  The caller owns every buffer;
+ *     the library never allocates, frees or synchronizes in these calls.
+ *     Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns without waiting.
+ *   - Host-visible arguments are validated; a bad one returns a non-zero
+ *     vq_status and sets a thread-local message naming the field
+ *     (vq_last_error).  Device-resident contents (codes >= K, row-map
+ *     entries, expert ids out of range, non-finite values) cannot be checked
+ *     without a synchronization and are preconditions: violating them gives
+ *     undefined output but never an out-of-bounds access for codes (the code
+ *     is masked to bits) -- ids and row maps must be in range.
+ *   - A HIP launch error returns VQ_ERR_HIP with the runtime's message.
+ *   - Results are bit-reproducible run to run (no floating-point atomics).
+ *   - One codebook per tensor, shared by all its experts: codebooks are
+ *     replicated, never sliced ("gemma-4-26b-a4b-it-VQ-6.2bpw", section
+ *     "Multi-machine (exo) note").
+ */
+#ifndef VQ_H
+#define VQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VQ_ABI_VERSION 1
+
+typedef enum vq_status {
+    VQ_OK = 0,
+    VQ_ERR_INVALID_ARGUMENT = 1, /* a null pointer, a negative size, mismatched shapes */
+    VQ_ERR_UNSUPPORTED = 2,      /* a geometry or size the kernels do not handle      */
+    VQ_ERR_WORKSPACE = 3,        /* workspace missing or smaller than required        */
+    VQ_ERR_HIP = 4               /* the HIP runtime reported an error                 */
+} vq_status;
+
+typedef enum vq_dtype {
+    VQ_F32 = 0,  /* IEEE binary32 activations                     */
+    VQ_BF16 = 1  /* bfloat16 activations (bit patterns, uint16)   */
+} vq_dtype;
+
+/* One VQ linear tensor stacked over experts. */
+typedef struct vq_tensor {
+    int32_t rows;             /* logical out features per expert, >= 1          */
+    int32_t cols;             /* in features, a positive multiple of 64         */
+    int32_t d;                /* subvector length: 2, 4 or 8                    */
+    int32_t bits;             /* code width: 8..13                              */
+    int32_t K;                /* codebook entries: 1 <= K <= 2^bits, and the
+                                 fp16 codebook (K*d*2 bytes) must fit 64 KiB   */
+    int32_t n_experts;        /* >= 1 (1 for a plain linear layer)              */
+    int64_t n_stored;         /* stored rows in codes/scales; == n_experts*rows
+                                 when row_map is NULL                          */
+    const uint16_t *codebook; /* fp16 bits [K][d]                               */
+    const uint32_t *codes;    /* [n_stored][wpr]                                */
+    const uint16_t *scales;   /* fp16 bits [n_stored][cols/64]                  */
+    const int32_t *row_map;   /* [n_experts*rows]: stored row of logical row r
+                                 of expert e at [e*rows + r], or -1 when the row
+                                 is dead (skip-zero); NULL = dense, stored row
+                                 e*rows + r                                      */
+} vq_tensor;
+
+/* ---- housekeeping ---------------------------------------------------- */
+
+int32_t vq_abi_version(void);
+const char *vq_status_string(vq_status s);
+/* Message of the last failed call on this thread ("" if none). */
+const char *vq_last_error(void);
+
+/* Host-only checks of a descriptor (no GPU work). */
+vq_status vq_validate(const vq_tensor *W);
+
+/* ---- dequantize (exact) ---------------------------------------------- */
+
+/* w[r][c] = W_e[r][c] as fp32 for expert `expert`, dead rows +0.0.
+   The fp16 x fp16 product is exact in fp32, so the result is bit-identical
+   to any exact decode.  w: device [rows][cols] fp32. */
+vq_status vq_dequantize(const vq_tensor *W, int32_t expert, float *w, void *stream);
+
+/* ---- decode: one expert, a few tokens ---------------------------------- */
+
+/* y[n][r] = sum_c W_e[r][c] * x[n][c] for n < n_tokens (0..64), fp32 out.
+   x: [n_tokens][cols] in x_dtype; y: [n_tokens][rows] fp32.  Dead rows
+   write +0.0.  Bandwidth-bound path (HBM roofline). */
+vq_status vq_expert_gemv(const vq_tensor *W, int32_t expert, int32_t n_tokens,
+                         const void *x, vq_dtype x_dtype, float *y, void *stream);
+
+/* ---- prefill: grouped GEMM over experts ---------------------------------- */
+
+/* Rows of x are grouped by expert: rows [expert_offsets[e], expert_offsets[e+1])
+   use expert e.  y[i][r] = sum_c W_e[r][c] * x[i][c], fp32, dead rows +0.0.
+   expert_offsets: device int32 [n_experts+1], non-decreasing, from 0 to
+   n_x_rows.  x: [n_x_rows][cols]; y: [n_x_rows][rows].  MFMA path with
+   dequantised fp16 tiles.  workspace: device, at least
+   vq_expert_gemm_workspace_size() bytes, 256-byte aligned. */
+size_t vq_expert_gemm_workspace_size(const vq_tensor *W, int32_t n_x_rows);
+vq_status vq_expert_gemm(const vq_tensor *W, int32_t n_x_rows, const void *x, vq_dtype x_dtype,
+                         const int32_t *expert_offsets, float *y,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---- the routed SwiGLU expert FFN ----------------------------------------- */
+
+/* For each token t and slot s < top_k with expert e = topk_ids[t][s]:
+     g = W_gate_e x_t,  u = W_up_e x_t,  h = silu(g) * u  (silu(z) = z/(1+e^-z)),
+     y[t] = sum_s topk_weights[t][s] * (W_down_e h).
+   Shapes: gate, up: rows = inter, cols = hidden; down: rows = hidden,
+   cols = inter; all three share n_experts.  x: [n_tokens][hidden] in
+   x_dtype; topk_ids int32 and topk_weights fp32 [n_tokens][top_k];
+   y: [n_tokens][hidden] fp32.  n_tokens <= 16 takes the bandwidth-bound
+   decode kernels, larger batches the grouped MFMA GEMM.  workspace: device,
+   at least vq_moe_ffn_workspace_size() bytes, 256-byte aligned. */
+size_t vq_moe_ffn_workspace_size(const vq_tensor *gate, const vq_tensor *up,
+                                 const vq_tensor *down, int32_t n_tokens, int32_t top_k);
+vq_status vq_moe_ffn(const vq_tensor *gate, const vq_tensor *up, const vq_tensor *down,
+                     int32_t n_tokens, int32_t top_k, const void *x, vq_dtype x_dtype,
+                     const int32_t *topk_ids, const float *topk_weights, float *y,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VQ_H */

@@ -1,0 +1,123 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/vq.h declares, and rejects bad host-visible arguments with the
+documented status and a message naming the field.  Only host validation
+runs here (the pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import vq_dequant_matmul_amd as vq
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "vq.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return vq.load_library()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vq_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_function_is_exported(lib):
+    names = _declared_functions()
+    assert "vq_moe_ffn" in names and "vq_expert_gemv" in names and "vq_expert_gemm" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in vq.h but not exported"
+
+
+def test_abi_version(lib):
+    assert lib.vq_abi_version() == 1
+
+
+FAKE = 0x10000  # never dereferenced: validation fails or succeeds on host values only
+
+
+def _t(**kw):
+    base = dict(rows=64, cols=128, d=4, bits=9, K=512, n_experts=2, n_stored=128,
+                codebook=FAKE, codes=FAKE, scales=FAKE, row_map=None)
+    base.update(kw)
+    return vq._CTensor(base["rows"], base["cols"], base["d"], base["bits"], base["K"],
+                       base["n_experts"], base["n_stored"], base["codebook"], base["codes"],
+                       base["scales"], base["row_map"])
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    ({}, 0, ""),
+    (dict(cols=100), 1, "cols"),
+    (dict(cols=0), 1, "cols"),
+    (dict(rows=0), 1, "rows"),
+    (dict(d=3), 2, "d = 3"),
+    (dict(bits=7, K=128), 2, "bits"),
+    (dict(bits=14), 2, "bits"),
+    (dict(K=513), 1, "K"),
+    (dict(K=0), 1, "K"),
+    (dict(d=8, bits=13, K=8192), 2, "codebook"),   # 128 KiB codebook > 64 KiB
+    (dict(n_experts=0), 1, "n_experts"),
+    (dict(codes=None), 1, "non-NULL"),
+    (dict(n_stored=100), 1, "n_stored"),
+    (dict(row_map=FAKE, n_stored=129), 1, "n_stored"),
+    (dict(codebook=FAKE + 2), 1, "aligned"),
+])
+def test_validate(lib, kw, status, needle):
+    t = _t(**kw)
+    st = lib.vq_validate(ctypes.byref(t))
+    assert st == status
+    if status:
+        assert needle in lib.vq_last_error().decode()
+        assert lib.vq_status_string(st).decode().startswith("VQ_ERR_")
+
+
+def test_validate_accepts_skipzero_and_k8192_d4(lib):
+    assert lib.vq_validate(ctypes.byref(_t(row_map=FAKE, n_stored=100))) == 0
+    assert lib.vq_validate(ctypes.byref(_t(bits=13, K=8192))) == 0
+
+
+def test_gemv_argument_errors(lib):
+    t = _t()
+    st = lib.vq_expert_gemv(ctypes.byref(t), 5, 1, FAKE, 1, FAKE, None)
+    assert st == 1 and "expert" in lib.vq_last_error().decode()
+    st = lib.vq_expert_gemv(ctypes.byref(t), 0, 65, FAKE, 1, FAKE, None)
+    assert st == 1 and "n_tokens" in lib.vq_last_error().decode()
+    st = lib.vq_expert_gemv(ctypes.byref(t), 0, 1, FAKE, 7, FAKE, None)
+    assert st == 1 and "x_dtype" in lib.vq_last_error().decode()
+    st = lib.vq_expert_gemv(ctypes.byref(t), 0, 1, FAKE + 4, 1, FAKE, None)
+    assert st == 1 and "x:" in lib.vq_last_error().decode()
+    # zero tokens is a no-op
+    assert lib.vq_expert_gemv(ctypes.byref(t), 0, 0, None, 1, None, None) == 0
+
+
+def test_moe_ffn_shape_and_workspace_errors(lib):
+    g = _t(rows=64, cols=128)
+    u = _t(rows=64, cols=128)
+    dn = _t(rows=128, cols=64, K=512, n_stored=256)
+    ok = lib.vq_moe_ffn_workspace_size(ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), 2, 2)
+    assert ok > 0
+    bad_dn = _t(rows=64, cols=128)
+    st = lib.vq_moe_ffn(ctypes.byref(g), ctypes.byref(u), ctypes.byref(bad_dn), 2, 2, FAKE, 1,
+                        FAKE, FAKE, FAKE, FAKE, ok, None)
+    assert st == 1 and "down" in lib.vq_last_error().decode()
+    st = lib.vq_moe_ffn(ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), 2, 3, FAKE, 1,
+                        FAKE, FAKE, FAKE, FAKE, ok, None)
+    assert st == 1 and "top_k" in lib.vq_last_error().decode()
+    st = lib.vq_moe_ffn(ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), 2, 2, FAKE, 1,
+                        FAKE, FAKE, FAKE, FAKE, ok - 1, None)
+    assert st == 3 and "workspace" in lib.vq_last_error().decode()
+    u2 = _t(rows=64, cols=128, bits=10, K=1024)
+    st = lib.vq_moe_ffn(ctypes.byref(g), ctypes.byref(u2), ctypes.byref(dn), 2, 2, FAKE, 1,
+                        FAKE, FAKE, FAKE, FAKE, ok, None)
+    assert st == 2 and "share d and bits" in lib.vq_last_error().decode()
+
+
+def test_binding_refuses_without_gpu():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    with pytest.raises(RuntimeError, match="GPU"):
+        vq._require_gpu()

@@ -1,0 +1,407 @@
+// vq_api.cpp -- the C ABI: argument validation, workspace sizing, dispatch.
+//
+// Errors follow the convention of the card "gemma-4-26b-a4b-it-VQ-6.2bpw"
+// (section "Multi-machine (exo) note"): a misuse fails loudly with an
+// explanatory message instead of producing plausible garbage.  Every check
+// here is on host-visible values; device-resident contents are documented
+// preconditions in vq.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/vq.h"
+#include "vq_internal.hpp"
+
+#define VQ_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+vq_status fail(vq_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+
+vq_status fail(vq_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+vq_status ok()
+{
+    g_last_error.clear();
+    return VQ_OK;
+}
+
+vq_status hip_fail(hipError_t e, const char *what)
+{
+    return fail(VQ_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t words_per_row(const vq_tensor &t)
+{
+    const int64_t n_sub = t.cols / t.d;
+    return ((n_sub + 31) / 32) * (int64_t)t.bits;
+}
+
+vq_status check_tensor(const vq_tensor *t, const char *name)
+{
+    if (!t)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "%s: descriptor is NULL", name);
+    if (t->rows < 1)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "%s.rows = %d: must be >= 1", name, t->rows);
+    if (t->cols < 64 || t->cols % 64 != 0)
+        return fail(VQ_ERR_INVALID_ARGUMENT,
+                    "%s.cols = %d: must be a positive multiple of 64 (one fp16 scale per 64 weights)",
+                    name, t->cols);
+    if (t->d != 2 && t->d != 4 && t->d != 8)
+        return fail(VQ_ERR_UNSUPPORTED, "%s.d = %d: supported subvector lengths are 2, 4 and 8",
+                    name, t->d);
+    if (t->bits < 8 || t->bits > 13)
+        return fail(VQ_ERR_UNSUPPORTED, "%s.bits = %d: supported code widths are 8..13", name,
+                    t->bits);
+    if (t->K < 1 || (int64_t)t->K > ((int64_t)1 << t->bits))
+        return fail(VQ_ERR_INVALID_ARGUMENT, "%s.K = %d: need 1 <= K <= 2^bits = %lld", name,
+                    t->K, (long long)(1LL << t->bits));
+    if ((int64_t)t->K * t->d * 2 > vq::kMaxCodebookBytes)
+        return fail(VQ_ERR_UNSUPPORTED,
+                    "%s: codebook of %lld bytes exceeds the %d-byte LDS budget per tensor", name,
+                    (long long)t->K * t->d * 2, vq::kMaxCodebookBytes);
+    if (t->n_experts < 1)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "%s.n_experts = %d: must be >= 1", name,
+                    t->n_experts);
+    if (!t->codebook || !t->codes || !t->scales)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "%s: codebook, codes and scales must be non-NULL",
+                    name);
+    if (!aligned(t->codebook, 4) || !aligned(t->codes, 4) || !aligned(t->scales, 2) ||
+        !aligned(t->row_map, 4))
+        return fail(VQ_ERR_INVALID_ARGUMENT,
+                    "%s: codebook/codes/row_map must be 4-byte and scales 2-byte aligned", name);
+    const int64_t full = (int64_t)t->n_experts * t->rows;
+    if (!t->row_map && t->n_stored != full)
+        return fail(VQ_ERR_INVALID_ARGUMENT,
+                    "%s.n_stored = %lld: a dense tensor (row_map NULL) stores n_experts*rows = %lld rows",
+                    name, (long long)t->n_stored, (long long)full);
+    if (t->row_map && (t->n_stored < 0 || t->n_stored > full))
+        return fail(VQ_ERR_INVALID_ARGUMENT, "%s.n_stored = %lld: must be in [0, n_experts*rows]",
+                    name, (long long)t->n_stored);
+    if (words_per_row(*t) * t->n_stored > ((int64_t)1 << 40))
+        return fail(VQ_ERR_UNSUPPORTED, "%s: tensor too large", name);
+    return VQ_OK;
+}
+
+vq_status check_dtype(vq_dtype dt)
+{
+    if (dt != VQ_F32 && dt != VQ_BF16)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "x_dtype = %d: must be VQ_F32 or VQ_BF16", (int)dt);
+    return VQ_OK;
+}
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct DecodeWs {
+    size_t h_off, z_off, total;
+};
+
+DecodeWs decode_ws(const vq_tensor &g, const vq_tensor &dn, int n_tok, int top_k)
+{
+    DecodeWs w;
+    const size_t pairs = (size_t)n_tok * top_k;
+    w.h_off = 0;
+    w.z_off = align_up(pairs * g.rows * sizeof(float), 256);
+    w.total = w.z_off + align_up(pairs * dn.rows * sizeof(float), 256);
+    return w;
+}
+
+constexpr int kDecodeMaxTokens = 16;
+constexpr int kGemvMaxTokens = 64;
+
+}  // namespace
+
+namespace vq {
+
+TensorDev to_dev(const vq_tensor &t)
+{
+    TensorDev d;
+    d.codes = t.codes;
+    d.scales = t.scales;
+    d.codebook = t.codebook;
+    d.row_map = t.row_map;
+    d.rows = t.rows;
+    d.cols = t.cols;
+    d.d = t.d;
+    d.bits = t.bits;
+    d.K = t.K;
+    d.n_experts = t.n_experts;
+    d.groups = t.cols / 64;
+    d.wpr = (int)words_per_row(t);
+    d.cb_dwords = t.K * t.d / 2;
+    return d;
+}
+
+}  // namespace vq
+
+// ------------------------------------------------------------------------------------
+// housekeeping
+// ------------------------------------------------------------------------------------
+
+VQ_EXPORT int32_t vq_abi_version(void) { return VQ_ABI_VERSION; }
+
+VQ_EXPORT const char *vq_status_string(vq_status s)
+{
+    switch (s) {
+    case VQ_OK: return "VQ_OK";
+    case VQ_ERR_INVALID_ARGUMENT: return "VQ_ERR_INVALID_ARGUMENT";
+    case VQ_ERR_UNSUPPORTED: return "VQ_ERR_UNSUPPORTED";
+    case VQ_ERR_WORKSPACE: return "VQ_ERR_WORKSPACE";
+    case VQ_ERR_HIP: return "VQ_ERR_HIP";
+    }
+    return "VQ_ERR_UNKNOWN";
+}
+
+VQ_EXPORT const char *vq_last_error(void) { return g_last_error.c_str(); }
+
+VQ_EXPORT vq_status vq_validate(const vq_tensor *W)
+{
+    vq_status st = check_tensor(W, "W");
+    return st != VQ_OK ? st : ok();
+}
+
+// ------------------------------------------------------------------------------------
+// dequantize
+// ------------------------------------------------------------------------------------
+
+VQ_EXPORT vq_status vq_dequantize(const vq_tensor *W, int32_t expert, float *w, void *stream)
+{
+    vq_status st = check_tensor(W, "W");
+    if (st != VQ_OK)
+        return st;
+    if (expert < 0 || expert >= W->n_experts)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "expert = %d: must be in [0, %d)", expert,
+                    W->n_experts);
+    if (!w || !aligned(w, 16))
+        return fail(VQ_ERR_INVALID_ARGUMENT, "w: must be a non-NULL, 16-byte aligned device pointer");
+    hipError_t e = vq::launch_dequantize(vq::to_dev(*W), expert, w, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "vq_dequantize");
+}
+
+// ------------------------------------------------------------------------------------
+// decode: one expert
+// ------------------------------------------------------------------------------------
+
+VQ_EXPORT vq_status vq_expert_gemv(const vq_tensor *W, int32_t expert, int32_t n_tokens,
+                                   const void *x, vq_dtype x_dtype, float *y, void *stream)
+{
+    vq_status st = check_tensor(W, "W");
+    if (st != VQ_OK)
+        return st;
+    if ((st = check_dtype(x_dtype)) != VQ_OK)
+        return st;
+    if (expert < 0 || expert >= W->n_experts)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "expert = %d: must be in [0, %d)", expert,
+                    W->n_experts);
+    if (n_tokens < 0 || n_tokens > kGemvMaxTokens)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "n_tokens = %d: must be in [0, %d]", n_tokens,
+                    kGemvMaxTokens);
+    if (W->cols / 64 > vq::kMaxGroupsDecode)
+        return fail(VQ_ERR_UNSUPPORTED, "W.cols = %d: the decode kernels take at most %d columns",
+                    W->cols, 64 * vq::kMaxGroupsDecode);
+    if (n_tokens == 0)
+        return ok();
+    if (!x || !aligned(x, 16))
+        return fail(VQ_ERR_INVALID_ARGUMENT, "x: must be a non-NULL, 16-byte aligned device pointer");
+    if (!y || !aligned(y, 4))
+        return fail(VQ_ERR_INVALID_ARGUMENT, "y: must be a non-NULL, 4-byte aligned device pointer");
+    vq::RowsLaunch L = {};
+    L.t[0] = vq::to_dev(*W);
+    L.nproj = 1;
+    L.act = x;
+    L.act_f32 = x_dtype == VQ_F32;
+    L.act_stride = W->cols;
+    L.out = y;
+    L.out_stride = W->rows;
+    L.expert = expert;
+    L.n_act = n_tokens;
+    hipError_t e = vq::launch_rows(L, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "vq_expert_gemv");
+}
+
+// ------------------------------------------------------------------------------------
+// prefill: grouped GEMM
+// ------------------------------------------------------------------------------------
+
+VQ_EXPORT size_t vq_expert_gemm_workspace_size(const vq_tensor *W, int32_t n_x_rows)
+{
+    if (check_tensor(W, "W") != VQ_OK || n_x_rows < 0)
+        return 0;
+    return vq::gemm_workspace_bytes(vq::to_dev(*W), n_x_rows);
+}
+
+VQ_EXPORT vq_status vq_expert_gemm(const vq_tensor *W, int32_t n_x_rows, const void *x,
+                                   vq_dtype x_dtype, const int32_t *expert_offsets, float *y,
+                                   void *workspace, size_t workspace_bytes, void *stream)
+{
+    vq_status st = check_tensor(W, "W");
+    if (st != VQ_OK)
+        return st;
+    if ((st = check_dtype(x_dtype)) != VQ_OK)
+        return st;
+    if (n_x_rows < 0)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "n_x_rows = %d: must be >= 0", n_x_rows);
+    if (n_x_rows == 0)
+        return ok();
+    if (!x || !aligned(x, 16))
+        return fail(VQ_ERR_INVALID_ARGUMENT, "x: must be a non-NULL, 16-byte aligned device pointer");
+    if (!y || !aligned(y, 16))
+        return fail(VQ_ERR_INVALID_ARGUMENT, "y: must be a non-NULL, 16-byte aligned device pointer");
+    if (!expert_offsets)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "expert_offsets: must be non-NULL");
+    const vq::TensorDev td = vq::to_dev(*W);
+    const size_t need = vq::gemm_workspace_bytes(td, n_x_rows);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+        return fail(VQ_ERR_WORKSPACE,
+                    "workspace: need %zu bytes, 256-byte aligned (got %zu bytes at %p)", need,
+                    workspace_bytes, workspace);
+    hipError_t e = vq::launch_expert_gemm(td, n_x_rows, x, x_dtype == VQ_F32, expert_offsets, y,
+                                          workspace, static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported)
+        return fail(VQ_ERR_UNSUPPORTED, "vq_expert_gemm: geometry not supported by the MFMA path");
+    return e == hipSuccess ? ok() : hip_fail(e, "vq_expert_gemm");
+}
+
+// ------------------------------------------------------------------------------------
+// routed SwiGLU FFN
+// ------------------------------------------------------------------------------------
+
+static vq_status check_ffn(const vq_tensor *gate, const vq_tensor *up, const vq_tensor *down,
+                           int32_t n_tokens, int32_t top_k)
+{
+    vq_status st;
+    if ((st = check_tensor(gate, "gate")) != VQ_OK || (st = check_tensor(up, "up")) != VQ_OK ||
+        (st = check_tensor(down, "down")) != VQ_OK)
+        return st;
+    if (up->rows != gate->rows || up->cols != gate->cols)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "up is %dx%d but gate is %dx%d", up->rows, up->cols,
+                    gate->rows, gate->cols);
+    if (down->rows != gate->cols || down->cols != gate->rows)
+        return fail(VQ_ERR_INVALID_ARGUMENT,
+                    "down is %dx%d: must be hidden x inter = %dx%d", down->rows, down->cols,
+                    gate->cols, gate->rows);
+    if (up->n_experts != gate->n_experts || down->n_experts != gate->n_experts)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "gate/up/down must have the same n_experts");
+    if (up->d != gate->d || up->bits != gate->bits)
+        return fail(VQ_ERR_UNSUPPORTED,
+                    "gate and up must share d and bits (they run in one fused kernel)");
+    if (n_tokens < 0)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "n_tokens = %d: must be >= 0", n_tokens);
+    if (top_k < 1 || top_k > gate->n_experts)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "top_k = %d: must be in [1, n_experts = %d]", top_k,
+                    gate->n_experts);
+    return VQ_OK;
+}
+
+VQ_EXPORT size_t vq_moe_ffn_workspace_size(const vq_tensor *gate, const vq_tensor *up,
+                                           const vq_tensor *down, int32_t n_tokens, int32_t top_k)
+{
+    if (check_ffn(gate, up, down, n_tokens, top_k) != VQ_OK)
+        return 0;
+    if (n_tokens <= kDecodeMaxTokens)
+        return decode_ws(*gate, *down, n_tokens, top_k).total;
+    return vq::moe_prefill_workspace_bytes(vq::to_dev(*gate), vq::to_dev(*up), vq::to_dev(*down),
+                                           n_tokens, top_k);
+}
+
+VQ_EXPORT vq_status vq_moe_ffn(const vq_tensor *gate, const vq_tensor *up, const vq_tensor *down,
+                               int32_t n_tokens, int32_t top_k, const void *x, vq_dtype x_dtype,
+                               const int32_t *topk_ids, const float *topk_weights, float *y,
+                               void *workspace, size_t workspace_bytes, void *stream)
+{
+    vq_status st = check_ffn(gate, up, down, n_tokens, top_k);
+    if (st != VQ_OK)
+        return st;
+    if ((st = check_dtype(x_dtype)) != VQ_OK)
+        return st;
+    if (n_tokens == 0)
+        return ok();
+    if (!x || !aligned(x, 16))
+        return fail(VQ_ERR_INVALID_ARGUMENT, "x: must be a non-NULL, 16-byte aligned device pointer");
+    if (!topk_ids || !topk_weights)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "topk_ids and topk_weights must be non-NULL");
+    if (!y || !aligned(y, 16))
+        return fail(VQ_ERR_INVALID_ARGUMENT, "y: must be a non-NULL, 16-byte aligned device pointer");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const vq::TensorDev g = vq::to_dev(*gate), u = vq::to_dev(*up), dn = vq::to_dev(*down);
+
+    if (n_tokens > kDecodeMaxTokens) {
+        const size_t need = vq::moe_prefill_workspace_bytes(g, u, dn, n_tokens, top_k);
+        if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+            return fail(VQ_ERR_WORKSPACE,
+                        "workspace: need %zu bytes, 256-byte aligned (got %zu bytes at %p)", need,
+                        workspace_bytes, workspace);
+        hipError_t e = vq::launch_moe_prefill(g, u, dn, n_tokens, top_k, x, x_dtype == VQ_F32,
+                                              topk_ids, topk_weights, y, workspace, s);
+        if (e == hipErrorNotSupported)
+            return fail(VQ_ERR_UNSUPPORTED, "vq_moe_ffn: geometry not supported by the MFMA path");
+        return e == hipSuccess ? ok() : hip_fail(e, "vq_moe_ffn (prefill)");
+    }
+
+    // ---- decode: gate+up+SwiGLU -> down -> slot-ordered combine ------------------
+    if (gate->cols / 64 > vq::kMaxGroupsDecode || down->cols / 64 > vq::kMaxGroupsDecode)
+        return fail(VQ_ERR_UNSUPPORTED, "the decode kernels take at most %d columns",
+                    64 * vq::kMaxGroupsDecode);
+    const int n_slots = n_tokens * top_k;
+    if (n_slots > vq::kMaxSlots)
+        return fail(VQ_ERR_UNSUPPORTED, "n_tokens * top_k = %d exceeds %d", n_slots,
+                    vq::kMaxSlots);
+    const DecodeWs ws = decode_ws(*gate, *down, n_tokens, top_k);
+    if (!workspace || workspace_bytes < ws.total || !aligned(workspace, 256))
+        return fail(VQ_ERR_WORKSPACE,
+                    "workspace: need %zu bytes, 256-byte aligned (got %zu bytes at %p)", ws.total,
+                    workspace_bytes, workspace);
+    float *h = reinterpret_cast<float *>(static_cast<char *>(workspace) + ws.h_off);
+    float *z = reinterpret_cast<float *>(static_cast<char *>(workspace) + ws.z_off);
+
+    vq::RowsLaunch L = {};
+    L.t[0] = g;
+    L.t[1] = u;
+    L.nproj = 2;
+    L.act = x;
+    L.act_f32 = x_dtype == VQ_F32;
+    L.act_stride = gate->cols;
+    L.out = h;
+    L.out_stride = gate->rows;
+    L.ids = topk_ids;
+    L.n_slots = n_slots;
+    L.act_div = top_k;
+    L.multi_per_expert = n_tokens > 1;
+    hipError_t e = vq::launch_rows(L, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "vq_moe_ffn (gate/up)");
+
+    vq::RowsLaunch D = {};
+    D.t[0] = dn;
+    D.nproj = 1;
+    D.act = h;
+    D.act_f32 = 1;
+    D.act_stride = gate->rows;
+    D.out = z;
+    D.out_stride = down->rows;
+    D.ids = topk_ids;
+    D.n_slots = n_slots;
+    D.act_div = 1;
+    D.multi_per_expert = n_tokens > 1;
+    e = vq::launch_rows(D, s);
+    if (e != hipSuccess)
+        return hip_fail(e, "vq_moe_ffn (down)");
+
+    e = vq::launch_combine(z, topk_weights, n_tokens, top_k, down->rows, y, s);
+    return e == hipSuccess ? ok() : hip_fail(e, "vq_moe_ffn (combine)");
+}

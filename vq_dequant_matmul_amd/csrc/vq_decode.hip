@@ -1,0 +1,147 @@
+// vq_decode.hip -- bandwidth-bound VQ kernels for small token counts (gfx950).
+//
+// The decode step of a VQ MoE layer reads every routed expert's packed codes
+// and scales once and does a handful of flops per byte, so it is bound by
+// HBM bandwidth (the card "GLM-5.3-Flash-VQ-2.7bpw", section "Limitations",
+// calls small-M decode the open frontier of the lineup; the card
+// "Qwen3.8-Flash-Next-VQ-4.4bpw", changelog 2026-09, reports its Metal expert
+// kernels being reworked for occupancy, direct activation reads and a SIMD
+// reduction).  Layout of the work here:
+//
+//   * a wavefront is split into segments of S lanes (S = a power of two
+//     >= the number of 64-column groups of a row, up to 64); a segment owns
+//     one output row per iteration and each lane owns whole groups of it
+//     (GPL groups per lane when a row has more than 64 groups);
+//   * a lane's activations for its groups stay in registers for every row it
+//     visits, as fp16 pairs scaled by a power of two chosen per (token,
+//     group) so the conversion from bf16 is exact;
+//   * codes are loaded as the few dwords that cover the lane's group and
+//     shifted to bit 0 with v_alignbit; code t sits at the compile-time bit
+//     t*b;  the tensor's codebook is staged once per workgroup in LDS;
+//   * each code contributes dot2(codebook entry, x pair) in fp32 and the
+//     group's fp16 scale is applied once per group (the scale factors out of
+//     the group's sum);  the segment's partial sums meet in a butterfly.
+//
+// The same engine runs one expert (vq_expert_gemv), the routed gate+up
+// projections with the SwiGLU product fused in the epilogue, and the routed
+// down projection.  Routed launches take one grid row per (token, slot)
+// pair; a workgroup whose pair is not the first occurrence of its expert
+// exits at once, the first occurrence serves every pair routed to that
+// expert, so each expert's weights are streamed exactly once.
+#include "vq_decode_impl.hpp"
+
+namespace vq {
+
+// Per-subvector-length instantiations live in vq_decode_d{2,4,8}.hip so they
+// compile in parallel.
+#define VQ_DECL_D(N)                                                                         \
+    extern template hipError_t rows_d<N>(int, const RowsArgs &, int, int, bool, bool, dim3, \
+                                         size_t, hipStream_t);                               \
+    extern template hipError_t dequantize_d<N>(const TensorDev &, int, float *, hipStream_t);
+VQ_DECL_D(2)
+VQ_DECL_D(4)
+VQ_DECL_D(8)
+#undef VQ_DECL_D
+
+// --------------------------------------------------------------------------------
+// combine: y[t][c] = sum over slots s (in order) of w[t][s] * z[t*k + s][c]
+// --------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ z,
+                                                 const float *__restrict__ w, int n_tok, int top_k,
+                                                 int hidden, float *__restrict__ y)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t n4 = (int64_t)n_tok * hidden / 4;
+    if (i >= n4)
+        return;
+    const int64_t t = (i * 4) / hidden;
+    const int64_t c = (i * 4) % hidden;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < top_k; ++s) {
+        const float ws = w[t * top_k + s];
+        const float4 v = *reinterpret_cast<const float4 *>(z + (t * top_k + s) * hidden + c);
+        acc.x += ws * v.x;
+        acc.y += ws * v.y;
+        acc.z += ws * v.z;
+        acc.w += ws * v.w;
+    }
+    *reinterpret_cast<float4 *>(y + t * hidden + c) = acc;
+}
+
+
+hipError_t launch_combine(const float *z, const float *w, int n_tok, int top_k, int hidden,
+                          float *y, hipStream_t stream)
+{
+    const int64_t n4 = (int64_t)n_tok * hidden / 4;
+    if (n4 == 0)
+        return hipSuccess;
+    const int blocks = (int)((n4 + 255) / 256);
+    hipLaunchKernelGGL(k_combine, dim3(blocks), dim3(256), 0, stream, z, w, n_tok, top_k, hidden, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream)
+{
+    const TensorDev &t0 = L.t[0];
+    const int gpl = (t0.groups + 63) / 64;
+    if (gpl > 2)
+        return hipErrorInvalidValue;
+    const int per_lane = (t0.groups + gpl - 1) / gpl;
+    int s_log2 = 0;
+    while ((1 << s_log2) < per_lane)
+        ++s_log2;
+    const int rpw = 64 >> s_log2;
+    RowsArgs a = {};
+    int off = 0;
+    for (int p = 0; p < L.nproj; ++p) {
+        a.codes[p] = L.t[p].codes;
+        a.scales[p] = L.t[p].scales;
+        a.row_map[p] = L.t[p].row_map;
+        a.codebook[p] = L.t[p].codebook;
+        a.cb_dwords[p] = L.t[p].cb_dwords;
+        a.cb_offset[p] = off;
+        off += (L.t[p].cb_dwords + 3) & ~3;
+    }
+    a.rows = t0.rows;
+    a.groups = t0.groups;
+    a.wpr = t0.wpr;
+    a.S_log2 = s_log2;
+    a.tile_rows = kWaves * kIters * rpw;
+    a.act = L.act;
+    a.act_stride = L.act_stride;
+    a.out = L.out;
+    a.out_stride = L.out_stride;
+    a.expert = L.expert;
+    a.n_act = L.n_act;
+    a.ids = L.ids;
+    a.n_slots = L.n_slots;
+    a.act_div = L.act_div > 0 ? L.act_div : 1;
+    const int n_y = L.ids ? L.n_slots : 1;
+    if ((L.ids ? L.n_slots : L.n_act) == 0 || t0.rows == 0)
+        return hipSuccess;
+    dim3 grid((t0.rows + a.tile_rows - 1) / a.tile_rows, n_y);
+    const size_t lds = (size_t)off * 4;
+    // more than one activation row per expert is possible only if the work
+    // list can hold several items for one expert
+    const bool multi = L.ids ? (L.multi_per_expert != 0) : (L.n_act > 1);
+    switch (t0.d) {
+    case 2: return rows_d<2>(t0.bits, a, gpl, L.nproj, L.act_f32 != 0, multi, grid, lds, stream);
+    case 4: return rows_d<4>(t0.bits, a, gpl, L.nproj, L.act_f32 != 0, multi, grid, lds, stream);
+    case 8: return rows_d<8>(t0.bits, a, gpl, L.nproj, L.act_f32 != 0, multi, grid, lds, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_dequantize(const TensorDev &t, int e, float *w, hipStream_t stream)
+{
+    if ((int64_t)t.rows * t.groups == 0)
+        return hipSuccess;
+    switch (t.d) {
+    case 2: return dequantize_d<2>(t, e, w, stream);
+    case 4: return dequantize_d<4>(t, e, w, stream);
+    case 8: return dequantize_d<8>(t, e, w, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace vq

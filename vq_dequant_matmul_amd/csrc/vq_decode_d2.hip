@@ -1,0 +1,10 @@
+// vq_decode_d2.hip -- decode-engine instantiations for d = 2.
+#include "vq_decode_impl.hpp"
+
+namespace vq {
+
+template hipError_t rows_d<2>(int, const RowsArgs &, int, int, bool, bool, dim3, size_t,
+                               hipStream_t);
+template hipError_t dequantize_d<2>(const TensorDev &, int, float *, hipStream_t);
+
+}  // namespace vq

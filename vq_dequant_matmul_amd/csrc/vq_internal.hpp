@@ -1,0 +1,75 @@
+// vq_internal.hpp -- host-side interface between the C ABI layer and the
+// kernel launchers.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/vq.h"
+
+namespace vq {
+
+// A tensor's device pointers and derived sizes.
+struct TensorDev {
+    const uint32_t *codes;
+    const uint16_t *scales;
+    const uint16_t *codebook;
+    const int32_t *row_map;
+    int rows, cols, d, bits, K, n_experts;
+    int groups;      // cols / 64
+    int wpr;         // words per stored row
+    int cb_dwords;   // K * d / 2
+};
+
+TensorDev to_dev(const vq_tensor &t);
+
+// Decode-engine work description (one launch).
+struct RowsLaunch {
+    TensorDev t[2];        // one or two projections (gate, up)
+    int nproj;             // 1 or 2 (2 = SwiGLU of t[0] (gate) and t[1] (up))
+    const void *act;       // activations: rows of t[0].cols elements
+    int act_f32;           // 1: fp32 activations, 0: bf16 bit patterns
+    int64_t act_stride;    // elements between activation rows
+    float *out;            // output rows
+    int64_t out_stride;    // elements between output rows
+    // work list: either one expert applied to n_act activation rows ...
+    int expert;
+    int n_act;
+    // ... or routed slots: pair q (< n_slots) uses expert ids[q]; its
+    // activation row is q / act_div (act_div = top_k for token inputs, 1
+    // for per-pair inputs) and its output row is q.
+    const int32_t *ids;
+    int n_slots;
+    int act_div;
+    // set when one expert may serve several pairs of the list (more than one
+    // token, or repeated ids within a token); selects the multi-row kernel
+    int multi_per_expert;
+};
+
+hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream);
+
+// y[t][c] = sum_s w[t][s] * z[t*k + s][c], slot order.
+hipError_t launch_combine(const float *z, const float *w, int n_tok, int top_k, int hidden,
+                          float *y, hipStream_t stream);
+
+hipError_t launch_dequantize(const TensorDev &t, int expert, float *w, hipStream_t stream);
+
+// Prefill (MFMA) path.
+struct GemmLaunch;
+size_t gemm_workspace_bytes(const TensorDev &t, int n_x_rows);
+hipError_t launch_expert_gemm(const TensorDev &t, int n_x_rows, const void *x, int x_f32,
+                              const int32_t *expert_offsets, float *y, void *ws,
+                              hipStream_t stream);
+size_t moe_prefill_workspace_bytes(const TensorDev &g, const TensorDev &u, const TensorDev &dn,
+                                   int n_tok, int top_k);
+hipError_t launch_moe_prefill(const TensorDev &g, const TensorDev &u, const TensorDev &dn,
+                              int n_tok, int top_k, const void *x, int x_f32,
+                              const int32_t *ids, const float *w, float *y, void *ws,
+                              hipStream_t stream);
+
+// Limits of the decode engine.
+constexpr int kMaxSlots = 1024;      // n_tokens * top_k in one routed launch
+constexpr int kMaxGroupsDecode = 128; // cols <= 8192
+constexpr int kMaxCodebookBytes = 65536;
+
+}  // namespace vq

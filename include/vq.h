@@ -136,7 +136,8 @@ vq_status vq_expert_gemm(const vq_tensor *W, int32_t n_x_rows, const void *x, vq
    cols = inter; all three share n_experts.  x: [n_tokens][hidden] in
    x_dtype; topk_ids int32 and topk_weights fp32 [n_tokens][top_k];
    y: [n_tokens][hidden] fp32.  n_tokens <= 16 takes the bandwidth-bound
-   decode kernels, larger batches the grouped MFMA GEMM.  workspace: device,
+   decode kernels (the three stages below, in order), larger batches the
+   grouped MFMA GEMM.  workspace: device,
    at least vq_moe_ffn_workspace_size() bytes, 256-byte aligned. */
 size_t vq_moe_ffn_workspace_size(const vq_tensor *gate, const vq_tensor *up,
                                  const vq_tensor *down, int32_t n_tokens, int32_t top_k);
@@ -144,6 +145,29 @@ vq_status vq_moe_ffn(const vq_tensor *gate, const vq_tensor *up, const vq_tensor
                      int32_t n_tokens, int32_t top_k, const void *x, vq_dtype x_dtype,
                      const int32_t *topk_ids, const float *topk_weights, float *y,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---- the three stages of the small-batch FFN, callable one by one -------- */
+
+/* Stage 1 (gate, up, SwiGLU): for pair q = t*top_k + s with e = topk_ids[t][s],
+     h[q][r] = silu(g) * u,  g = (W_gate_e x_t)[r],  u = (W_up_e x_t)[r];
+   a row dead in gate or in up gives h = +0.0.  Each routed expert's weights
+   are read once however many pairs it serves.  n_tokens*top_k <= 1024;
+   h: device fp32 [n_tokens*top_k][inter]. */
+vq_status vq_moe_gate_up(const vq_tensor *gate, const vq_tensor *up, int32_t n_tokens,
+                         int32_t top_k, const void *x, vq_dtype x_dtype,
+                         const int32_t *topk_ids, float *h, void *stream);
+
+/* Stage 2 (down): z[q][c] = sum_r W_down_e[c][r] * h[q][r] for every pair q;
+   dead rows of down give +0.0.  h: device fp32 [n_tokens*top_k][inter];
+   z: device fp32 [n_tokens*top_k][hidden]. */
+vq_status vq_moe_down(const vq_tensor *down, int32_t n_tokens, int32_t top_k, const float *h,
+                      const int32_t *topk_ids, float *z, void *stream);
+
+/* Stage 3 (combine): y[t][c] = sum over s in slot order of
+   topk_weights[t][s] * z[t*top_k + s][c].  z, y: device fp32, 16-byte
+   aligned; hidden a multiple of 4. */
+vq_status vq_moe_combine(int32_t n_tokens, int32_t top_k, int32_t hidden, const float *z,
+                         const float *topk_weights, float *y, void *stream);
 
 #ifdef __cplusplus
 }

@@ -72,6 +72,9 @@ def load_library():
         "vq_expert_gemm": (ctypes.c_int, [T, I32, P, ctypes.c_int, P, P, P, SZ, P]),
         "vq_moe_ffn_workspace_size": (SZ, [T, T, T, I32, I32]),
         "vq_moe_ffn": (ctypes.c_int, [T, T, T, I32, I32, P, ctypes.c_int, P, P, P, P, SZ, P]),
+        "vq_moe_gate_up": (ctypes.c_int, [T, T, I32, I32, P, ctypes.c_int, P, P, P]),
+        "vq_moe_down": (ctypes.c_int, [T, I32, I32, P, P, P, P]),
+        "vq_moe_combine": (ctypes.c_int, [I32, I32, I32, P, P, P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -261,8 +264,52 @@ def vq_moe_ffn(gate: VQTensor, up: VQTensor, down: VQTensor, x: torch.Tensor,
     return out
 
 
+def vq_moe_gate_up(gate: VQTensor, up: VQTensor, x: torch.Tensor, topk_ids: torch.Tensor,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """h[t*top_k + s] = silu(W_gate_e x_t) * (W_up_e x_t), e = topk_ids[t, s]."""
+    _require_gpu()
+    lib = load_library()
+    x = x.contiguous()
+    n, k = topk_ids.shape
+    if out is None:
+        out = torch.empty((n * k, gate.rows), dtype=torch.float32, device=x.device)
+    g, u = gate.c(), up.c()
+    _check(lib.vq_moe_gate_up(ctypes.byref(g), ctypes.byref(u), n, k, _ptr(x), _x_dtype(x),
+                              _ptr(topk_ids.contiguous()), _ptr(out), _stream()))
+    return out
+
+
+def vq_moe_down(down: VQTensor, h: torch.Tensor, topk_ids: torch.Tensor,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """z[q] = W_down_e h[q] for every (token, slot) pair q."""
+    _require_gpu()
+    lib = load_library()
+    n, k = topk_ids.shape
+    if out is None:
+        out = torch.empty((n * k, down.rows), dtype=torch.float32, device=h.device)
+    dc = down.c()
+    _check(lib.vq_moe_down(ctypes.byref(dc), n, k, _ptr(h.contiguous()),
+                           _ptr(topk_ids.contiguous()), _ptr(out), _stream()))
+    return out
+
+
+def vq_moe_combine(z: torch.Tensor, topk_weights: torch.Tensor,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[t] = sum over slots s of topk_weights[t, s] * z[t*top_k + s]."""
+    _require_gpu()
+    lib = load_library()
+    n, k = topk_weights.shape
+    hidden = z.shape[1]
+    if out is None:
+        out = torch.empty((n, hidden), dtype=torch.float32, device=z.device)
+    _check(lib.vq_moe_combine(n, k, hidden, _ptr(z.contiguous()),
+                              _ptr(topk_weights.contiguous()), _ptr(out), _stream()))
+    return out
+
+
 __all__ = [
     "VQError", "VQTensor", "build", "load_library", "vq_validate", "vq_dequantize",
     "vq_expert_gemv", "vq_expert_gemm", "vq_expert_gemm_workspace_size", "vq_moe_ffn",
-    "vq_moe_ffn_workspace_size", "VQ_F32", "VQ_BF16",
+    "vq_moe_ffn_workspace_size", "vq_moe_gate_up", "vq_moe_down", "vq_moe_combine",
+    "VQ_F32", "VQ_BF16",
 ]

@@ -141,6 +141,7 @@ TensorDev to_dev(const vq_tensor &t)
     d.bits = t.bits;
     d.K = t.K;
     d.n_experts = t.n_experts;
+    d.n_stored = t.n_stored;
     d.groups = t.cols / 64;
     d.wpr = (int)words_per_row(t);
     d.cb_dwords = t.K * t.d / 2;
@@ -281,6 +282,58 @@ VQ_EXPORT vq_status vq_expert_gemm(const vq_tensor *W, int32_t n_x_rows, const v
 // routed SwiGLU FFN
 // ------------------------------------------------------------------------------------
 
+static vq_status check_decode_sizes(const vq_tensor &a, const vq_tensor &b, int32_t n_tokens,
+                                    int32_t top_k)
+{
+    if (n_tokens < 0)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "n_tokens = %d: must be >= 0", n_tokens);
+    if (a.cols / 64 > vq::kMaxGroupsDecode || b.cols / 64 > vq::kMaxGroupsDecode)
+        return fail(VQ_ERR_UNSUPPORTED, "the decode kernels take at most %d columns",
+                    64 * vq::kMaxGroupsDecode);
+    if ((int64_t)n_tokens * top_k > vq::kMaxSlots)
+        return fail(VQ_ERR_UNSUPPORTED, "n_tokens * top_k = %lld exceeds %d",
+                    (long long)n_tokens * top_k, vq::kMaxSlots);
+    return VQ_OK;
+}
+
+static hipError_t launch_gate_up(const vq::TensorDev &g, const vq::TensorDev &u, int n_tokens,
+                                 int top_k, const void *x, bool x_f32, const int32_t *ids,
+                                 float *h, hipStream_t s)
+{
+    vq::RowsLaunch L = {};
+    L.t[0] = g;
+    L.t[1] = u;
+    L.nproj = 2;
+    L.act = x;
+    L.act_f32 = x_f32;
+    L.act_stride = g.cols;
+    L.out = h;
+    L.out_stride = g.rows;
+    L.ids = ids;
+    L.n_slots = n_tokens * top_k;
+    L.act_div = top_k;
+    L.multi_per_expert = n_tokens > 1;
+    return vq::launch_rows(L, s);
+}
+
+static hipError_t launch_down(const vq::TensorDev &dn, int n_tokens, int top_k, const float *h,
+                              const int32_t *ids, float *z, hipStream_t s)
+{
+    vq::RowsLaunch L = {};
+    L.t[0] = dn;
+    L.nproj = 1;
+    L.act = h;
+    L.act_f32 = 1;
+    L.act_stride = dn.cols;
+    L.out = z;
+    L.out_stride = dn.rows;
+    L.ids = ids;
+    L.n_slots = n_tokens * top_k;
+    L.act_div = 1;
+    L.multi_per_expert = n_tokens > 1;
+    return vq::launch_rows(L, s);
+}
+
 static vq_status check_ffn(const vq_tensor *gate, const vq_tensor *up, const vq_tensor *down,
                            int32_t n_tokens, int32_t top_k)
 {
@@ -354,13 +407,8 @@ VQ_EXPORT vq_status vq_moe_ffn(const vq_tensor *gate, const vq_tensor *up, const
     }
 
     // ---- decode: gate+up+SwiGLU -> down -> slot-ordered combine ------------------
-    if (gate->cols / 64 > vq::kMaxGroupsDecode || down->cols / 64 > vq::kMaxGroupsDecode)
-        return fail(VQ_ERR_UNSUPPORTED, "the decode kernels take at most %d columns",
-                    64 * vq::kMaxGroupsDecode);
-    const int n_slots = n_tokens * top_k;
-    if (n_slots > vq::kMaxSlots)
-        return fail(VQ_ERR_UNSUPPORTED, "n_tokens * top_k = %d exceeds %d", n_slots,
-                    vq::kMaxSlots);
+    if ((st = check_decode_sizes(*gate, *down, n_tokens, top_k)) != VQ_OK)
+        return st;
     const DecodeWs ws = decode_ws(*gate, *down, n_tokens, top_k);
     if (!workspace || workspace_bytes < ws.total || !aligned(workspace, 256))
         return fail(VQ_ERR_WORKSPACE,
@@ -368,40 +416,79 @@ VQ_EXPORT vq_status vq_moe_ffn(const vq_tensor *gate, const vq_tensor *up, const
                     workspace_bytes, workspace);
     float *h = reinterpret_cast<float *>(static_cast<char *>(workspace) + ws.h_off);
     float *z = reinterpret_cast<float *>(static_cast<char *>(workspace) + ws.z_off);
-
-    vq::RowsLaunch L = {};
-    L.t[0] = g;
-    L.t[1] = u;
-    L.nproj = 2;
-    L.act = x;
-    L.act_f32 = x_dtype == VQ_F32;
-    L.act_stride = gate->cols;
-    L.out = h;
-    L.out_stride = gate->rows;
-    L.ids = topk_ids;
-    L.n_slots = n_slots;
-    L.act_div = top_k;
-    L.multi_per_expert = n_tokens > 1;
-    hipError_t e = vq::launch_rows(L, s);
+    hipError_t e = launch_gate_up(g, u, n_tokens, top_k, x, x_dtype == VQ_F32, topk_ids, h, s);
     if (e != hipSuccess)
         return hip_fail(e, "vq_moe_ffn (gate/up)");
-
-    vq::RowsLaunch D = {};
-    D.t[0] = dn;
-    D.nproj = 1;
-    D.act = h;
-    D.act_f32 = 1;
-    D.act_stride = gate->rows;
-    D.out = z;
-    D.out_stride = down->rows;
-    D.ids = topk_ids;
-    D.n_slots = n_slots;
-    D.act_div = 1;
-    D.multi_per_expert = n_tokens > 1;
-    e = vq::launch_rows(D, s);
+    e = launch_down(dn, n_tokens, top_k, h, topk_ids, z, s);
     if (e != hipSuccess)
         return hip_fail(e, "vq_moe_ffn (down)");
-
     e = vq::launch_combine(z, topk_weights, n_tokens, top_k, down->rows, y, s);
     return e == hipSuccess ? ok() : hip_fail(e, "vq_moe_ffn (combine)");
+}
+
+VQ_EXPORT vq_status vq_moe_gate_up(const vq_tensor *gate, const vq_tensor *up, int32_t n_tokens,
+                                   int32_t top_k, const void *x, vq_dtype x_dtype,
+                                   const int32_t *topk_ids, float *h, void *stream)
+{
+    vq_status st;
+    if ((st = check_tensor(gate, "gate")) != VQ_OK || (st = check_tensor(up, "up")) != VQ_OK)
+        return st;
+    if (up->rows != gate->rows || up->cols != gate->cols || up->n_experts != gate->n_experts)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "up must match gate's shape and n_experts");
+    if (up->d != gate->d || up->bits != gate->bits)
+        return fail(VQ_ERR_UNSUPPORTED,
+                    "gate and up must share d and bits (they run in one fused kernel)");
+    if ((st = check_dtype(x_dtype)) != VQ_OK)
+        return st;
+    if (top_k < 1 || top_k > gate->n_experts)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "top_k = %d: must be in [1, n_experts = %d]", top_k,
+                    gate->n_experts);
+    if ((st = check_decode_sizes(*gate, *gate, n_tokens, top_k)) != VQ_OK)
+        return st;
+    if (n_tokens == 0)
+        return ok();
+    if (!x || !aligned(x, 16) || !topk_ids || !h || !aligned(h, 4))
+        return fail(VQ_ERR_INVALID_ARGUMENT,
+                    "x (16-byte aligned), topk_ids and h must be non-NULL device pointers");
+    hipError_t e = launch_gate_up(vq::to_dev(*gate), vq::to_dev(*up), n_tokens, top_k, x,
+                                  x_dtype == VQ_F32, topk_ids, h, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "vq_moe_gate_up");
+}
+
+VQ_EXPORT vq_status vq_moe_down(const vq_tensor *down, int32_t n_tokens, int32_t top_k,
+                                const float *h, const int32_t *topk_ids, float *z, void *stream)
+{
+    vq_status st;
+    if ((st = check_tensor(down, "down")) != VQ_OK)
+        return st;
+    if (top_k < 1 || top_k > down->n_experts)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "top_k = %d: must be in [1, n_experts = %d]", top_k,
+                    down->n_experts);
+    if ((st = check_decode_sizes(*down, *down, n_tokens, top_k)) != VQ_OK)
+        return st;
+    if (n_tokens == 0)
+        return ok();
+    if (!h || !aligned(h, 16) || !topk_ids || !z || !aligned(z, 4))
+        return fail(VQ_ERR_INVALID_ARGUMENT,
+                    "h (16-byte aligned), topk_ids and z must be non-NULL device pointers");
+    hipError_t e = launch_down(vq::to_dev(*down), n_tokens, top_k, h, topk_ids, z,
+                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "vq_moe_down");
+}
+
+VQ_EXPORT vq_status vq_moe_combine(int32_t n_tokens, int32_t top_k, int32_t hidden, const float *z,
+                                   const float *topk_weights, float *y, void *stream)
+{
+    if (n_tokens < 0 || top_k < 1 || hidden < 0 || hidden % 4 != 0)
+        return fail(VQ_ERR_INVALID_ARGUMENT,
+                    "n_tokens = %d, top_k = %d, hidden = %d: need n_tokens >= 0, top_k >= 1, "
+                    "hidden a multiple of 4", n_tokens, top_k, hidden);
+    if (n_tokens == 0 || hidden == 0)
+        return ok();
+    if (!z || !aligned(z, 16) || !y || !aligned(y, 16) || !topk_weights)
+        return fail(VQ_ERR_INVALID_ARGUMENT,
+                    "z and y (16-byte aligned) and topk_weights must be non-NULL device pointers");
+    hipError_t e = vq::launch_combine(z, topk_weights, n_tokens, top_k, hidden, y,
+                                      static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "vq_moe_combine");
 }

@@ -45,6 +45,16 @@ struct Geom {
     static constexpr int NW = (OMAX + GB + 31) / 32;   // words loaded per group
     static constexpr uint32_t MASK = (BITS == 32) ? 0xffffffffu : ((1u << BITS) - 1u);
     static constexpr int ENTRY_WORDS = D / 2;          // fp16 codebook entry, in dwords
+    // true if the NW words of some group would run past the end of its
+    // 32-code block (then the last row's loads must be clamped)
+    static constexpr bool overruns()
+    {
+        for (int q = 0; q < GPB; ++q)
+            if (((q * GB) >> 5) + NW > BITS)
+                return true;
+        return false;
+    }
+    static constexpr bool CLAMP = overruns();
 };
 
 // Word offset (inside the row) and bit offset of group g.

@@ -35,8 +35,8 @@ namespace vq {
 // Per-subvector-length instantiations live in vq_decode_d{2,4,8}.hip so they
 // compile in parallel.
 #define VQ_DECL_D(N)                                                                         \
-    extern template hipError_t rows_d<N>(int, const RowsArgs &, int, int, bool, bool, dim3, \
-                                         size_t, hipStream_t);                               \
+    extern template hipError_t rows_d<N>(int, const RowsArgs &, int, int, bool, int64_t, int, \
+                                         size_t, hipStream_t);                                \
     extern template hipError_t dequantize_d<N>(const TensorDev &, int, float *, hipStream_t);
 VQ_DECL_D(2)
 VQ_DECL_D(4)
@@ -57,6 +57,8 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ z,
     const int64_t t = (i * 4) / hidden;
     const int64_t c = (i * 4) % hidden;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    // unrolled so the slots' loads are in flight together
+#pragma unroll 8
     for (int s = 0; s < top_k; ++s) {
         const float ws = w[t * top_k + s];
         const float4 v = *reinterpret_cast<const float4 *>(z + (t * top_k + s) * hidden + c);
@@ -80,6 +82,40 @@ hipError_t launch_combine(const float *z, const float *w, int n_tok, int top_k, 
     return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void k_fill_rows(float *__restrict__ out, int n_rows, int cols,
+                                                   int64_t stride)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < (int64_t)n_rows * cols)
+        out[(i / cols) * stride + i % cols] = 0.0f;
+}
+
+static hipError_t launch_fill_rows(float *out, int n_rows, int cols, int64_t stride,
+                                   hipStream_t stream)
+{
+    const int64_t n = (int64_t)n_rows * cols;
+    hipLaunchKernelGGL(k_fill_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, out,
+                       n_rows, cols, stride);
+    return hipGetLastError();
+}
+
+// The device's CU count (queried once per device).
+static int cu_count()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream)
 {
     const TensorDev &t0 = L.t[0];
@@ -92,21 +128,19 @@ hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream)
         ++s_log2;
     const int rpw = 64 >> s_log2;
     RowsArgs a = {};
-    int off = 0;
     for (int p = 0; p < L.nproj; ++p) {
         a.codes[p] = L.t[p].codes;
         a.scales[p] = L.t[p].scales;
         a.row_map[p] = L.t[p].row_map;
         a.codebook[p] = L.t[p].codebook;
         a.cb_dwords[p] = L.t[p].cb_dwords;
-        a.cb_offset[p] = off;
-        off += (L.t[p].cb_dwords + 3) & ~3;
     }
     a.rows = t0.rows;
     a.groups = t0.groups;
     a.wpr = t0.wpr;
     a.S_log2 = s_log2;
     a.tile_rows = kWaves * kIters * rpw;
+    a.tiles = (t0.rows + a.tile_rows - 1) / a.tile_rows;
     a.act = L.act;
     a.act_stride = L.act_stride;
     a.out = L.out;
@@ -115,19 +149,35 @@ hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream)
     a.n_act = L.n_act;
     a.ids = L.ids;
     a.n_slots = L.n_slots;
-    a.act_div = L.act_div > 0 ? L.act_div : 1;
-    const int n_y = L.ids ? L.n_slots : 1;
-    if ((L.ids ? L.n_slots : L.n_act) == 0 || t0.rows == 0)
+    a.act_div = (L.ids && L.act_div > 0) ? L.act_div : 1;
+    const int P = L.ids ? L.n_slots : L.n_act;
+    if (P == 0 || t0.rows == 0)
         return hipSuccess;
-    dim3 grid((t0.rows + a.tile_rows - 1) / a.tile_rows, n_y);
+    // a projection whose rows are all dead (skip-zero) stores nothing: every
+    // output row it touches is exactly zero (for SwiGLU, silu(0)*u = 0 and
+    // silu(g)*0 = 0 are written as +0.0)
+    for (int p = 0; p < L.nproj; ++p)
+        if (L.t[p].n_stored == 0)
+            return launch_fill_rows(L.out, P, t0.rows, L.out_stride, stream);
+
+    // LDS: codebook 0 at dword 0; codebook 1 at 2^bits*d/2 dwords when that
+    // offset is at most 32 KiB (the kernel then uses it as a constant), else
+    // right after codebook 0; the work lists last
+    a.cb_offset[0] = 0;
+    const int cb1_fixed = (1 << t0.bits) * t0.d / 2;
+    a.cb_offset[1] = (cb1_fixed * 4 <= 32768) ? cb1_fixed : ((L.t[0].cb_dwords + 3) & ~3);
+    int off = L.nproj == 2 ? a.cb_offset[1] + L.t[1].cb_dwords : L.t[0].cb_dwords;
+    off = (off + 3) & ~3;
+    a.list_offset = off;
+    off += list_dwords(P);
     const size_t lds = (size_t)off * 4;
-    // more than one activation row per expert is possible only if the work
-    // list can hold several items for one expert
-    const bool multi = L.ids ? (L.multi_per_expert != 0) : (L.n_act > 1);
+
+    const int64_t units = (int64_t)P * a.tiles;
+    const int n_cu = cu_count();
     switch (t0.d) {
-    case 2: return rows_d<2>(t0.bits, a, gpl, L.nproj, L.act_f32 != 0, multi, grid, lds, stream);
-    case 4: return rows_d<4>(t0.bits, a, gpl, L.nproj, L.act_f32 != 0, multi, grid, lds, stream);
-    case 8: return rows_d<8>(t0.bits, a, gpl, L.nproj, L.act_f32 != 0, multi, grid, lds, stream);
+    case 2: return rows_d<2>(t0.bits, a, gpl, L.nproj, L.act_f32 != 0, units, n_cu, lds, stream);
+    case 4: return rows_d<4>(t0.bits, a, gpl, L.nproj, L.act_f32 != 0, units, n_cu, lds, stream);
+    case 8: return rows_d<8>(t0.bits, a, gpl, L.nproj, L.act_f32 != 0, units, n_cu, lds, stream);
     default: return hipErrorInvalidValue;
     }
 }

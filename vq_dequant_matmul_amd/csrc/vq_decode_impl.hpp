@@ -24,10 +24,12 @@
 //
 // The same engine runs one expert (vq_expert_gemv), the routed gate+up
 // projections with the SwiGLU product fused in the epilogue, and the routed
-// down projection.  Routed launches take one grid row per (token, slot)
-// pair; a workgroup whose pair is not the first occurrence of its expert
-// exits at once, the first occurrence serves every pair routed to that
-// expert, so each expert's weights are streamed exactly once.
+// down projection.  It is persistent: a few workgroups per CU each stage the
+// codebooks and build the routing lists once (the (token, slot) pairs
+// grouped by distinct expert, in slot order), then walk a contiguous range
+// of work units.  A unit is (distinct expert, tile of rows, one of its
+// pairs), ordered expert-major, so consecutive units of a workgroup share
+// the pair's converted activations and usually the expert.
 #pragma once
 #include "vq_common.hpp"
 #include "vq_internal.hpp"
@@ -43,18 +45,41 @@ struct RowsArgs {
     const int32_t *row_map[2];
     const uint16_t *codebook[2];
     int cb_dwords[2];
-    int cb_offset[2];   // dword offset of each codebook in LDS
+    int cb_offset[2];   // dword offset of each codebook in LDS (0 and cb1_offset())
+    int list_offset;    // dword offset of the work lists in LDS
     int rows, groups, wpr;
-    int S_log2;         // segment size
-    int tile_rows;      // rows per workgroup
+    int S_log2;         // lanes per row segment
+    int tile_rows;      // rows per work unit
+    int tiles;          // tiles per expert
     const void *act;
     int64_t act_stride;
     float *out;
     int64_t out_stride;
-    int expert, n_act;
-    const int32_t *ids;
-    int n_slots, act_div;
+    int expert, n_act;  // one expert applied to n_act activation rows ...
+    const int32_t *ids; // ... or routed pairs: pair q uses expert ids[q],
+    int n_slots, act_div; // activation row q / act_div, output row q
 };
+
+// LDS layout of a workgroup (dwords, 16-byte aligned, nothing static):
+//   [0, ...)             codebook of projection 0 (lookups address code*d/2)
+//   [cb1_offset(), ...)  codebook of projection 1 (gate+up launches)
+//   [list_offset, ...)   work lists (see build_lists)
+// The second codebook sits at its largest possible size when that keeps
+// the offset inside a ds_read immediate, so no lookup needs a base add.
+template <int D, int BITS>
+constexpr int cb1_fixed_dwords() { return (1 << BITS) * D / 2; }
+
+template <int D, int BITS>
+constexpr bool cb1_is_fixed() { return cb1_fixed_dwords<D, BITS>() * 4 <= 32768; }
+
+template <int D, int BITS>
+__device__ __forceinline__ int cb1_offset(const RowsArgs &a)
+{
+    if constexpr (cb1_is_fixed<D, BITS>())
+        return cb1_fixed_dwords<D, BITS>();
+    else
+        return a.cb_offset[1];
+}
 
 template <int D>
 struct Entry {
@@ -94,63 +119,99 @@ __device__ __forceinline__ uint32_t extract(const uint32_t (&nw)[NW], int t)
     return __builtin_amdgcn_alignbit(nw[wi + 1], nw[wi], sh) & mask;
 }
 
-// Activations of one lane: NT rows x GPL groups x 32 fp16 pairs, plus the
-// factor 2^-k that undoes each (row, group)'s range scaling.
-template <int NT, int GPL, bool HL>
+// Activations of one lane for one row: GPL groups x 32 fp16 pairs, plus the
+// factor 2^-k that undoes each group's range scaling.
+template <int GPL, bool HL>
 struct XRegs {
-    f16x2 hi[NT][GPL][32];
-    f16x2 lo[HL ? NT : 1][HL ? GPL : 1][HL ? 32 : 1];
-    float m[NT][GPL];
+    f16x2 hi[GPL][32];
+    f16x2 lo[HL ? GPL : 1][HL ? 32 : 1];
+    float m[GPL];
 };
 
-template <bool F32>
-__device__ __forceinline__ void load_act64(const void *base, int64_t off, float (&v)[64])
+// Raw activations of one lane (bf16: 32 dwords per group, fp32: 64).
+template <int GPL, bool F32>
+struct XRaw {
+    static constexpr int Q = F32 ? 16 : 8;   // uint4 per group
+    uint4 q[GPL][Q];
+};
+
+template <int GPL, bool F32>
+__device__ __forceinline__ void load_x_raw(const RowsArgs &a, int arow, int sl, int S,
+                                           XRaw<GPL, F32> &xw)
 {
-    if constexpr (F32) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const float *>(base) + off);
+    constexpr int Q = XRaw<GPL, F32>::Q;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const uint4 q = p[i];
-            v[4 * i + 0] = __uint_as_float(q.x);
-            v[4 * i + 1] = __uint_as_float(q.y);
-            v[4 * i + 2] = __uint_as_float(q.z);
-            v[4 * i + 3] = __uint_as_float(q.w);
-        }
-    } else {
-        const uint4 *p = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + off);
+    for (int i = 0; i < GPL; ++i) {
+        // lanes past the last group read the last group (their result is
+        // discarded); every load is unconditional so all stay in flight
+        const int g = min(sl + i * S, a.groups - 1);
+        const int64_t off = (int64_t)arow * a.act_stride + 64 * g;
+        const uint4 *p = F32 ? reinterpret_cast<const uint4 *>(static_cast<const float *>(a.act) + off)
+                             : reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.act) + off);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint4 q = p[i];
-            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[8 * i + 2 * j + 0] = __uint_as_float(w[j] << 16);
-                v[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-            }
-        }
+        for (int j = 0; j < Q; ++j)
+            xw.q[i][j] = p[j];
     }
 }
 
-// Scale 64 activations by a power of two so they are fp16 normals, and split
-// into fp16 pairs (hi) plus, for fp32 sources, the fp16 residual (lo).
-template <bool HL>
-__device__ __forceinline__ float to_scaled_pairs(const float (&v)[64], f16x2 (&hi)[32],
-                                                 f16x2 (&lo)[HL ? 32 : 1])
+// Raw activations -> range-scaled fp16 pairs, one dword (bf16 pair) or two
+// floats at a time.  For bf16 the largest magnitude is found on the bit
+// patterns (non-negative floats order like their integer encodings).
+template <int GPL, bool HL, bool F32>
+__device__ __forceinline__ void convert_x(const XRaw<GPL, F32> &xw, XRegs<GPL, HL> &xr)
 {
-    float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 64; ++i)
-        amax = fmaxf(amax, fabsf(v[i]));
-    const int k = range_exponent(amax);
-    const float up = ldexpf(1.0f, k);
+    for (int i = 0; i < GPL; ++i) {
+        const uint4 *q = xw.q[i];
+        if constexpr (F32) {
+            float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const float a = v[2 * i] * up, b = v[2 * i + 1] * up;
-        hi[i] = pack_f16x2(a, b);
-        if constexpr (HL)
-            lo[i] = pack_f16x2(a - (float)hi[i].x, b - (float)hi[i].y);
+            for (int j = 0; j < 16; ++j)
+                amax = fmaxf(fmaxf(amax, fmaxf(fabsf(__uint_as_float(q[j].x)),
+                                               fabsf(__uint_as_float(q[j].y)))),
+                             fmaxf(fabsf(__uint_as_float(q[j].z)), fabsf(__uint_as_float(q[j].w))));
+            const int k = range_exponent(amax);
+            const float up = ldexpf(1.0f, k);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float f[4] = {__uint_as_float(q[j].x) * up, __uint_as_float(q[j].y) * up,
+                                    __uint_as_float(q[j].z) * up, __uint_as_float(q[j].w) * up};
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const f16x2 hp = pack_f16x2(f[2 * h], f[2 * h + 1]);
+                    xr.hi[i][2 * j + h] = hp;
+                    if constexpr (HL)
+                        xr.lo[i][2 * j + h] = pack_f16x2(f[2 * h] - (float)hp.x, f[2 * h + 1] - (float)hp.y);
+                }
+            }
+            xr.m[i] = ldexpf(1.0f, -k);
+        } else {
+            uint32_t mx = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t w4[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h)
+                    mx = max(mx, max(w4[h] & 0x7fffu, (w4[h] >> 16) & 0x7fffu));
+            }
+            const int k = range_exponent(__uint_as_float(mx << 16));
+            const float up = ldexpf(1.0f, k);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t w4[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const float lo16 = __uint_as_float(w4[h] << 16) * up;
+                    const float hi16 = __uint_as_float(w4[h] & 0xffff0000u) * up;
+                    const f16x2 hp = pack_f16x2(lo16, hi16);
+                    xr.hi[i][4 * j + h] = hp;
+                    if constexpr (HL)
+                        xr.lo[i][4 * j + h] = pack_f16x2(lo16 - (float)hp.x, hi16 - (float)hp.y);
+                }
+            }
+            xr.m[i] = ldexpf(1.0f, -k);
+        }
     }
-    return ldexpf(1.0f, -k);
 }
 
 template <int D, int BITS, int GPL, int NPROJ>
@@ -160,231 +221,370 @@ struct RowRegs {
     int live;   // bit p: projection p's row is stored (not skip-zero)
 };
 
-// Wave-level: list of the pairs routed to this workgroup's expert, or an
-// empty list when blockIdx.y is not the expert's first occurrence.
-__device__ __forceinline__ void build_pair_list(const int *__restrict__ s_ids, int n_slots, int q,
-                                                int *__restrict__ s_list, int *__restrict__ s_n)
-{
-    const int lane = threadIdx.x & 63;
-    const int e = s_ids[q];
-    bool dup = false;
-    for (int i = lane; i < q; i += 64)
-        dup |= (s_ids[i] == e);
-    if (__ballot(dup) != 0ull) {
-        if (lane == 0)
-            *s_n = 0;
-        return;
-    }
-    int n = 0;
-    for (int base = q; base < n_slots; base += 64) {
-        const int i = base + lane;
-        const bool m = (i < n_slots) && (s_ids[i] == e);
-        const unsigned long long b = __ballot(m);
-        if (m)
-            s_list[n + __popcll(b & ((1ull << lane) - 1ull))] = i;
-        n += __popcll(b);
-    }
-    if (lane == 0)
-        *s_n = n;
-}
-
-template <int D, int BITS, int GPL, int NPROJ, bool HL, bool F32, int ITERS, int NT>
-__device__ __forceinline__ void compute_chunk(const RowsArgs &a, const uint32_t *__restrict__ lds,
-                                              const RowRegs<D, BITS, GPL, NPROJ> (&rr)[ITERS],
-                                              const int *__restrict__ list, int c0, int e, int S,
-                                              int seg, int sl, int row0, int rpw)
+// Issue the code and scale loads of this lane's rows (every load
+// unconditional; rows past the end and dead rows read stored row 0 and are
+// zeroed afterwards -- the host never launches for a tensor with no stored
+// rows).  The stored-row lookup (row map) is one dependent load.
+template <int D, int BITS, int GPL, int NPROJ, int ITERS>
+__device__ __forceinline__ void load_rows(const RowsArgs &a, int e, int row0, int rpw, int seg,
+                                          int sl, int S, RowRegs<D, BITS, GPL, NPROJ> (&rr)[ITERS])
 {
     using GM = Geom<D, BITS>;
     constexpr int NW = GM::NW;
-    constexpr int G = GM::G;
-    constexpr int HP = D / 2;   // fp16 pairs per codebook entry
-    (void)e;
-
-    XRegs<NT, GPL, HL> xr;
-#pragma unroll
-    for (int n = 0; n < NT; ++n) {
-        const int item = list ? list[c0 + n] : c0 + n;
-        const int64_t arow = list ? (int64_t)(item / a.act_div) : (int64_t)item;
-#pragma unroll
-        for (int i = 0; i < GPL; ++i) {
-            const int g = sl + i * S;
-            if (g < a.groups) {
-                float v[64];
-                load_act64<F32>(a.act, arow * a.act_stride + 64 * g, v);
-                xr.m[n][i] = to_scaled_pairs<HL>(v, xr.hi[n][i], xr.lo[HL ? n : 0][HL ? i : 0]);
-            } else {
-                xr.m[n][i] = 0.0f;
-#pragma unroll
-                for (int t = 0; t < 32; ++t) {
-                    xr.hi[n][i][t] = f16x2{(f16)0.0f, (f16)0.0f};
-                    if constexpr (HL)
-                        xr.lo[n][i][t] = f16x2{(f16)0.0f, (f16)0.0f};
-                }
-            }
-        }
-    }
-
+    int srow[ITERS][NPROJ];
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
         const int r = row0 + it * rpw + seg;
-        float part[NT][NPROJ];
+        const int64_t lin = (int64_t)e * a.rows + min(r, a.rows - 1);
 #pragma unroll
-        for (int n = 0; n < NT; ++n)
-#pragma unroll
-            for (int p = 0; p < NPROJ; ++p)
-                part[n][p] = 0.0f;
-#pragma unroll
-        for (int p = 0; p < NPROJ; ++p) {
-            const uint32_t *cb = lds + a.cb_offset[p];
-#pragma unroll
-            for (int i = 0; i < GPL; ++i) {
-                const int g = sl + i * S;
-                uint32_t nw[NW];
-                shift_group_words<D, BITS>(g, rr[it].w[p][i], nw);
-                float acc[NT], accl[NT];
-#pragma unroll
-                for (int n = 0; n < NT; ++n) {
-                    acc[n] = 0.0f;
-                    accl[n] = 0.0f;
-                }
-#pragma unroll
-                for (int t = 0; t < G; ++t) {
-                    const uint32_t code = extract<BITS, NW>(nw, t);
-                    const Entry<D> en = fetch_entry<D>(cb, code);
-#pragma unroll
-                    for (int n = 0; n < NT; ++n)
-#pragma unroll
-                        for (int k = 0; k < HP; ++k) {
-                            acc[n] = dot2(en.v[k], xr.hi[n][i][t * HP + k], acc[n]);
-                            if constexpr (HL)
-                                accl[n] = dot2(en.v[k], xr.lo[n][i][t * HP + k], accl[n]);
-                        }
-                }
-                const float s = half_bits_to_float(rr[it].sc[p][i]);
-#pragma unroll
-                for (int n = 0; n < NT; ++n)
-                    part[n][p] += (HL ? acc[n] + accl[n] : acc[n]) * (s * xr.m[n][i]);
-            }
-        }
-        // segment butterfly (S is uniform)
-#pragma unroll
-        for (int n = 0; n < NT; ++n)
-#pragma unroll
-            for (int p = 0; p < NPROJ; ++p) {
-                float v = part[n][p];
-#pragma unroll
-                for (int m = 32; m >= 1; m >>= 1)
-                    if (m < S)
-                        v += __shfl_xor(v, m, 64);
-                part[n][p] = v;
-            }
-        if (sl == 0 && r < a.rows) {
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                const int item = list ? list[c0 + n] : c0 + n;
-                float val;
-                if constexpr (NPROJ == 2)
-                    val = (rr[it].live == 3) ? silu_mul(part[n][0], part[n][1]) : 0.0f;
-                else
-                    val = (rr[it].live & 1) ? part[n][0] : 0.0f;
-                a.out[(int64_t)item * a.out_stride + r] = val;
-            }
-        }
+        for (int p = 0; p < NPROJ; ++p)
+            srow[it][p] = a.row_map[p] ? a.row_map[p][lin] : (int)lin;
     }
-}
-
-template <int D, int BITS, int GPL, int NPROJ, bool HL, bool F32, int ITERS, int NTM>
-__global__ __launch_bounds__(kThreads) void k_rows(const RowsArgs a)
-{
-    using GM = Geom<D, BITS>;
-    constexpr int NW = GM::NW;
-    extern __shared__ uint32_t lds[];
-    __shared__ int s_ids[kMaxSlots];
-    __shared__ int s_list[kMaxSlots];
-    __shared__ int s_n;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-
-    // ---- work list ---------------------------------------------------------
-    int e, n_items;
-    const int *list = nullptr;
-    if (a.ids) {
-        for (int i = tid; i < a.n_slots; i += kThreads)
-            s_ids[i] = a.ids[i];
-        __syncthreads();
-        if (wave == 0)
-            build_pair_list(s_ids, a.n_slots, blockIdx.y, s_list, &s_n);
-        __syncthreads();
-        n_items = s_n;
-        if (n_items == 0)
-            return;
-        e = s_ids[blockIdx.y];
-        list = s_list;
-    } else {
-        e = a.expert;
-        n_items = a.n_act;
-    }
-
-    // ---- issue the loads of this wave's rows --------------------------------
-    const int S = 1 << a.S_log2;
-    const int rpw = 64 >> a.S_log2;
-    const int seg = lane >> a.S_log2;
-    const int sl = lane & (S - 1);
-    const int row0 = blockIdx.x * a.tile_rows + wave * ITERS * rpw;
-
-    RowRegs<D, BITS, GPL, NPROJ> rr[ITERS];
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
         const int r = row0 + it * rpw + seg;
         rr[it].live = 0;
 #pragma unroll
         for (int p = 0; p < NPROJ; ++p) {
-            int64_t s = -1;
-            if (r < a.rows)
-                s = stored_row(a.row_map[p], a.rows, e, r);
-            if (s >= 0)
-                rr[it].live |= 1 << p;
+            const bool live = (r < a.rows) && (srow[it][p] >= 0);
+            rr[it].live |= live ? (1 << p) : 0;
+            const int64_t sr = live ? srow[it][p] : 0;
+            const uint32_t *row = a.codes[p] + sr * a.wpr;
 #pragma unroll
             for (int i = 0; i < GPL; ++i) {
-                const int g = sl + i * S;
-                if (s >= 0 && g < a.groups) {
-                    load_group_raw<D, BITS>(a.codes[p] + s * a.wpr, g, rr[it].w[p][i]);
-                    rr[it].sc[p][i] = a.scales[p][s * a.groups + g];
-                } else {
+                const int g = min(sl + i * S, a.groups - 1);
+                const int w0 = (g * GM::GB) >> 5;
+                if constexpr (GM::CLAMP) {
 #pragma unroll
                     for (int k = 0; k < NW; ++k)
-                        rr[it].w[p][i][k] = 0u;
-                    rr[it].sc[p][i] = 0u;
+                        rr[it].w[p][i][k] = row[min(w0 + k, a.wpr - 1)];
+                } else {
+                    // the group's words never leave its block: 16-byte loads
+                    // (dword alignment suffices on gfx950)
+                    __builtin_memcpy(rr[it].w[p][i], row + w0, NW * 4);
                 }
+                rr[it].sc[p][i] = a.scales[p][sr * a.groups + g];
             }
         }
     }
+}
 
-    // ---- codebooks -> LDS ------------------------------------------------------
+template <int D, int BITS, int GPL, int NPROJ, bool HL, int ITERS>
+__device__ __forceinline__ void compute_rows(const RowsArgs &a, const uint32_t *__restrict__ lds,
+                                             const RowRegs<D, BITS, GPL, NPROJ> (&rr)[ITERS],
+                                             const XRegs<GPL, HL> &xr, int item, int S, int seg,
+                                             int sl, int row0, int rpw)
+{
+    using GM = Geom<D, BITS>;
+    constexpr int NW = GM::NW;
+    constexpr int G = GM::G;
+    constexpr int HP = D / 2;   // fp16 pairs per codebook entry
+
 #pragma unroll
-    for (int p = 0; p < NPROJ; ++p)
-        stage_codebook(lds + a.cb_offset[p], a.codebook[p], a.cb_dwords[p]);
-    __syncthreads();
-
-    // ---- activations in chunks of up to NTM rows -------------------------------
-    int c0 = 0;
-    while (c0 < n_items) {
-        const int left = n_items - c0;
-        if (NTM >= 4 && left >= 4) {
-            compute_chunk<D, BITS, GPL, NPROJ, HL, F32, ITERS, (NTM >= 4 ? 4 : 1)>(
-                a, lds, rr, list, c0, e, S, seg, sl, row0, rpw);
-            c0 += (NTM >= 4 ? 4 : 1);
-        } else if (NTM >= 2 && left >= 2) {
-            compute_chunk<D, BITS, GPL, NPROJ, HL, F32, ITERS, (NTM >= 2 ? 2 : 1)>(
-                a, lds, rr, list, c0, e, S, seg, sl, row0, rpw);
-            c0 += (NTM >= 2 ? 2 : 1);
-        } else {
-            compute_chunk<D, BITS, GPL, NPROJ, HL, F32, ITERS, 1>(a, lds, rr, list, c0, e, S,
-                                                                   seg, sl, row0, rpw);
-            c0 += 1;
+    for (int it = 0; it < ITERS; ++it) {
+        const int r = row0 + it * rpw + seg;
+        float part[NPROJ];
+#pragma unroll
+        for (int p = 0; p < NPROJ; ++p) {
+            part[p] = 0.0f;
+            const uint32_t *cb = lds + (p == 0 ? 0 : cb1_offset<D, BITS>(a));
+#pragma unroll
+            for (int i = 0; i < GPL; ++i) {
+                const int g = sl + i * S;
+                uint32_t nw[NW];
+                shift_group_words<D, BITS>(g, rr[it].w[p][i], nw);
+                float acc = 0.0f, accl = 0.0f;
+#pragma unroll
+                for (int t = 0; t < G; ++t) {
+                    const uint32_t code = extract<BITS, NW>(nw, t);
+                    const Entry<D> en = fetch_entry<D>(cb, code);
+#pragma unroll
+                    for (int k = 0; k < HP; ++k) {
+                        acc = dot2(en.v[k], xr.hi[i][t * HP + k], acc);
+                        if constexpr (HL)
+                            accl = dot2(en.v[k], xr.lo[i][t * HP + k], accl);
+                    }
+                }
+                const float s = (g < a.groups) ? half_bits_to_float(rr[it].sc[p][i]) : 0.0f;
+                part[p] += (HL ? acc + accl : acc) * (s * xr.m[i]);
+                // keep one group's lookups in flight at a time (bounds registers)
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
+        // segment butterfly (S is uniform)
+#pragma unroll
+        for (int p = 0; p < NPROJ; ++p) {
+            float v = part[p];
+#pragma unroll
+            for (int m = 32; m >= 1; m >>= 1)
+                if (m < S)
+                    v += __shfl_xor(v, m, 64);
+            part[p] = v;
+        }
+        if (sl == 0 && r < a.rows) {
+            float val;
+            if constexpr (NPROJ == 2)
+                val = (rr[it].live == 3) ? silu_mul(part[0], part[1]) : 0.0f;
+            else
+                val = (rr[it].live & 1) ? part[0] : 0.0f;
+            a.out[(int64_t)item * a.out_stride + r] = val;
+        }
+    }
+}
+
+// Codebook staging (layout above).  Up to CbBatch
+// uint4 per thread are loaded into registers together with everything else a
+// workgroup needs, then written to LDS; larger codebooks finish with a
+// looping pass.
+template <int D, int BITS>
+constexpr int cb_max_dwords() { return (1 << BITS) * D / 2; }
+
+template <int D, int BITS>
+constexpr int cb_batch()
+{
+    constexpr int per_thread = (cb_max_dwords<D, BITS>() / 4 + kThreads - 1) / kThreads;
+    return per_thread < 4 ? per_thread : 4;
+}
+
+template <int D, int BITS, int NPROJ>
+struct CbRegs {
+    uint4 v[NPROJ][cb_batch<D, BITS>()];
+};
+
+template <int D, int BITS, int NPROJ>
+__device__ __forceinline__ void load_codebooks(const RowsArgs &a, CbRegs<D, BITS, NPROJ> &cr)
+{
+    constexpr int B = cb_batch<D, BITS>();
+#pragma unroll
+    for (int p = 0; p < NPROJ; ++p) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.codebook[p]);
+        const int n4 = a.cb_dwords[p] >> 2;
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const int i = threadIdx.x + j * kThreads;
+            cr.v[p][j] = (i < n4) ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+}
+
+template <int D, int BITS, int NPROJ>
+__device__ __forceinline__ void store_codebooks(const RowsArgs &a, const CbRegs<D, BITS, NPROJ> &cr,
+                                                uint32_t *__restrict__ lds)
+{
+    constexpr int B = cb_batch<D, BITS>();
+#pragma unroll
+    for (int p = 0; p < NPROJ; ++p) {
+        uint32_t *base = lds + (p == 0 ? 0 : cb1_offset<D, BITS>(a));
+        uint4 *dst = reinterpret_cast<uint4 *>(base);
+        const int n4 = a.cb_dwords[p] >> 2;
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const int i = threadIdx.x + j * kThreads;
+            if (i < n4)
+                dst[i] = cr.v[p][j];
+        }
+        // the rest: codebooks beyond B*16*kThreads bytes, and a tail of fewer
+        // than four dwords
+        const uint32_t *s32 = reinterpret_cast<const uint32_t *>(a.codebook[p]);
+        for (int i = 4 * B * kThreads + threadIdx.x * 4; i + 3 < a.cb_dwords[p]; i += 4 * kThreads)
+            *reinterpret_cast<uint4 *>(base + i) = *reinterpret_cast<const uint4 *>(s32 + i);
+        for (int i = (n4 << 2) + threadIdx.x; i < a.cb_dwords[p]; i += kThreads)
+            base[i] = s32[i];
+    }
+}
+
+// Work lists in LDS, from list_offset (P = number of pairs):
+//   ids[P]      expert of each pair
+//   first[P]    first pair with the same expert
+//   rank[P]     position of the pair among its expert's pairs (slot order)
+//   uidx[P]     index of the pair's expert among the distinct experts
+//   ustart[P+1] start of each distinct expert's pairs in items[]
+//   items[P]    pairs grouped by distinct expert (first-occurrence order)
+//   uexp[P]     expert id of each distinct expert
+//   U           number of distinct experts
+// Everything is a deterministic function of the ids.
+struct Lists {
+    int *ids, *first, *rank, *uidx, *ustart, *items, *uexp, *U;
+};
+
+__device__ __forceinline__ Lists lists_at(uint32_t *lds, int offset, int P)
+{
+    Lists L;
+    L.ids = reinterpret_cast<int *>(lds + offset);
+    L.first = L.ids + P;
+    L.rank = L.first + P;
+    L.uidx = L.rank + P;
+    L.ustart = L.uidx + P;
+    L.items = L.ustart + P + 1;
+    L.uexp = L.items + P;
+    L.U = L.uexp + P;
+    return L;
+}
+
+constexpr int list_dwords(int P) { return 7 * P + 2; }
+
+// Called by every thread after L.ids is filled and a barrier.
+__device__ __forceinline__ void build_lists(const Lists &L, int P)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    for (int q = tid; q < P; q += kThreads) {
+        const int id = L.ids[q];
+        int f = q, r = 0;
+        for (int q2 = 0; q2 < q; ++q2)
+            if (L.ids[q2] == id) {
+                f = (r == 0) ? q2 : f;
+                ++r;
+            }
+        L.first[q] = f;
+        L.rank[q] = r;
+    }
+    for (int u = tid; u <= P; u += kThreads)
+        L.ustart[u] = 0;
+    __syncthreads();
+    if (tid < 64) {   // distinct experts in first-occurrence order
+        int base = 0;
+        for (int c = 0; c < P; c += 64) {
+            const int q = c + lane;
+            const bool isf = (q < P) && (L.first[q] == q);
+            const unsigned long long b = __ballot(isf);
+            if (isf) {
+                const int u = base + __popcll(b & ((1ull << lane) - 1ull));
+                L.uidx[q] = u;
+                L.uexp[u] = L.ids[q];
+            }
+            base += __popcll(b);
+        }
+        if (lane == 0)
+            *L.U = base;
+    }
+    __syncthreads();
+    for (int q = tid; q < P; q += kThreads)
+        atomicAdd(&L.ustart[L.uidx[L.first[q]] + 1], 1);
+    __syncthreads();
+    if (tid < 64) {   // prefix sum of the counts
+        const int U = *L.U;
+        int run = 0;
+        for (int c = 0; c < U; c += 64) {
+            const int u = c + lane;
+            int v = (u < U) ? L.ustart[u + 1] : 0;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(v, o, 64);
+                if (lane >= o)
+                    v += t;
+            }
+            if (u < U)
+                L.ustart[u + 1] = run + v;
+            run += __shfl(v, 63, 64);
+        }
+    }
+    __syncthreads();
+    for (int q = tid; q < P; q += kThreads)
+        L.items[L.ustart[L.uidx[L.first[q]]] + L.rank[q]] = q;
+    __syncthreads();
+}
+
+template <int D, int BITS, int GPL, int NPROJ, bool HL, bool F32, int ITERS>
+__global__ __launch_bounds__(kThreads) void k_rows(const RowsArgs a)
+{
+    // all LDS is dynamic so the first codebook starts at byte 0; 16-byte
+    // alignment keeps the 8- and 16-byte codebook entries aligned (a
+    // misaligned ds_read_b64 costs several times an aligned one)
+    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    // ---- setup: codebooks and work lists, once per workgroup -----------------
+    CbRegs<D, BITS, NPROJ> cr;
+    load_codebooks<D, BITS, NPROJ>(a, cr);
+    const int P = a.ids ? a.n_slots : a.n_act;
+    const Lists L = lists_at(lds, a.list_offset, P);
+    if (a.ids) {
+        for (int q = tid; q < P; q += kThreads)
+            L.ids[q] = a.ids[q];
+    } else {
+        for (int q = tid; q < P; q += kThreads) {
+            L.items[q] = q;
+            L.ids[q] = a.expert;
+        }
+        if (tid == 0) {
+            L.ustart[0] = 0;
+            L.ustart[1] = P;
+            L.uexp[0] = a.expert;
+            *L.U = 1;
+        }
+    }
+    store_codebooks<D, BITS, NPROJ>(a, cr, lds);
+    __syncthreads();
+    if (a.ids)
+        build_lists(L, P);
+
+    // ---- this workgroup's contiguous range of units (expert, tile, pair) -----
+    const int S = 1 << a.S_log2;
+    const int rpw = 64 >> a.S_log2;
+    const int seg = lane >> a.S_log2;
+    const int sl = lane & (S - 1);
+    const int64_t n_units = (int64_t)P * a.tiles;
+    int64_t k = (int64_t)blockIdx.x * n_units / gridDim.x;
+    const int64_t k_end = (int64_t)(blockIdx.x + 1) * n_units / gridDim.x;
+    // Units are software-pipelined two deep: the rows of unit k+1 are in
+    // flight while unit k is computed (buffers A and B alternate).
+    struct Unit {
+        int item, e, row0;
+    };
+    int u = 0;
+    auto unit_at = [&](int64_t kk) {
+        while (kk >= (int64_t)L.ustart[u + 1] * a.tiles)
+            ++u;
+        const int u0 = L.ustart[u];
+        const int nu = L.ustart[u + 1] - u0;
+        const int64_t rel = kk - (int64_t)u0 * a.tiles;
+        const int t = (int)(rel / nu);
+        Unit un;
+        un.item = L.items[u0 + (int)(rel - (int64_t)t * nu)];
+        un.e = L.uexp[u];
+        un.row0 = t * a.tile_rows + wave * ITERS * rpw;
+        return un;
+    };
+    int cur_item = -1;
+    XRegs<GPL, HL> xr;
+    auto run = [&](const Unit &un, const RowRegs<D, BITS, GPL, NPROJ>(&rr)[ITERS]) {
+        if (un.item != cur_item) {
+            XRaw<GPL, F32> xw;
+            load_x_raw<GPL, F32>(a, un.item / a.act_div, sl, S, xw);
+            convert_x<GPL, HL, F32>(xw, xr);
+            cur_item = un.item;
+        }
+        compute_rows<D, BITS, GPL, NPROJ, HL, ITERS>(a, lds, rr, xr, un.item, S, seg, sl, un.row0,
+                                                     rpw);
+    };
+    if (k >= k_end)
+        return;
+    RowRegs<D, BITS, GPL, NPROJ> A[ITERS], B[ITERS];
+    Unit ua = unit_at(k), ub;
+    load_rows<D, BITS, GPL, NPROJ, ITERS>(a, ua.e, ua.row0, rpw, seg, sl, S, A);
+    for (;;) {
+        const bool more_b = k + 1 < k_end;
+        if (more_b) {
+            ub = unit_at(k + 1);
+            load_rows<D, BITS, GPL, NPROJ, ITERS>(a, ub.e, ub.row0, rpw, seg, sl, S, B);
+        }
+        run(ua, A);
+        if (!more_b)
+            break;
+        ++k;
+        const bool more_a = k + 1 < k_end;
+        if (more_a) {
+            ua = unit_at(k + 1);
+            load_rows<D, BITS, GPL, NPROJ, ITERS>(a, ua.e, ua.row0, rpw, seg, sl, S, A);
+        }
+        run(ub, B);
+        if (!more_a)
+            break;
+        ++k;
     }
 }
 
@@ -466,10 +666,14 @@ hipError_t dequantize_d(const TensorDev &t, int e, float *w, hipStream_t s)
 
 constexpr int kIters = 2;
 
-template <int D, int BITS, int GPL, int NPROJ, bool HL, bool F32, int NTM>
-static hipError_t rows_launch(const RowsArgs &a, dim3 grid, size_t lds_bytes, hipStream_t stream)
+// The persistent grid is as many workgroups as can be resident at once
+// (occupancy of this instantiation at this LDS size, times the CU count),
+// capped by the number of work units.
+template <int D, int BITS, int GPL, int NPROJ, bool HL, bool F32>
+static hipError_t rows_launch(const RowsArgs &a, int64_t units, int n_cu, size_t lds_bytes,
+                              hipStream_t stream)
 {
-    auto kern = k_rows<D, BITS, GPL, NPROJ, HL, F32, kIters, NTM>;
+    auto kern = k_rows<D, BITS, GPL, NPROJ, HL, F32, kIters>;
     if (lds_bytes > 65536) {
         hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -477,52 +681,53 @@ static hipError_t rows_launch(const RowsArgs &a, dim3 grid, size_t lds_bytes, hi
         if (err != hipSuccess)
             return err;
     }
+    int per_cu = 0;
+    hipError_t err = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void *>(kern), kThreads, lds_bytes);
+    if (err != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    const int64_t cap = (int64_t)per_cu * n_cu;
+    const dim3 grid((unsigned)(units < cap ? units : cap));
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds_bytes, stream, a);
     return hipGetLastError();
 }
 
-// Token-chunk width: 1 when every expert serves one activation row, else up
-// to 4 rows per pass (fewer when the activations take more registers).
 template <int D, int BITS, int GPL, int NPROJ>
-static hipError_t rows_act(const RowsArgs &a, bool act_f32, bool multi, dim3 grid, size_t lds,
+static hipError_t rows_act(const RowsArgs &a, bool act_f32, int64_t units, int n_cu, size_t lds,
                            hipStream_t s)
 {
-    if (act_f32) {
-        if (multi)
-            return rows_launch<D, BITS, GPL, NPROJ, true, true, (GPL == 1 ? 2 : 1)>(a, grid, lds, s);
-        return rows_launch<D, BITS, GPL, NPROJ, true, true, 1>(a, grid, lds, s);
-    }
-    if (multi)
-        return rows_launch<D, BITS, GPL, NPROJ, false, false, (GPL == 1 ? 4 : 2)>(a, grid, lds, s);
-    return rows_launch<D, BITS, GPL, NPROJ, false, false, 1>(a, grid, lds, s);
+    // fp32 activations keep their low bits as a second fp16 term
+    if (act_f32)
+        return rows_launch<D, BITS, GPL, NPROJ, true, true>(a, units, n_cu, lds, s);
+    return rows_launch<D, BITS, GPL, NPROJ, false, false>(a, units, n_cu, lds, s);
 }
 
 template <int D, int BITS>
-static hipError_t rows_db(const RowsArgs &a, int gpl, int nproj, bool act_f32, bool multi,
-                          dim3 grid, size_t lds, hipStream_t s)
+static hipError_t rows_db(const RowsArgs &a, int gpl, int nproj, bool act_f32, int64_t units,
+                          int n_cu, size_t lds, hipStream_t s)
 {
     if (gpl == 1)
-        return nproj == 2 ? rows_act<D, BITS, 1, 2>(a, act_f32, multi, grid, lds, s)
-                          : rows_act<D, BITS, 1, 1>(a, act_f32, multi, grid, lds, s);
-    return nproj == 2 ? rows_act<D, BITS, 2, 2>(a, act_f32, multi, grid, lds, s)
-                      : rows_act<D, BITS, 2, 1>(a, act_f32, multi, grid, lds, s);
+        return nproj == 2 ? rows_act<D, BITS, 1, 2>(a, act_f32, units, n_cu, lds, s)
+                          : rows_act<D, BITS, 1, 1>(a, act_f32, units, n_cu, lds, s);
+    return nproj == 2 ? rows_act<D, BITS, 2, 2>(a, act_f32, units, n_cu, lds, s)
+                      : rows_act<D, BITS, 2, 1>(a, act_f32, units, n_cu, lds, s);
 }
 
 template <int D>
 struct RowsD {
     template <int BITS>
-    static hipError_t run(const RowsArgs &a, int gpl, int nproj, bool f32, bool multi, dim3 grid,
+    static hipError_t run(const RowsArgs &a, int gpl, int nproj, bool f32, int64_t units, int n_cu,
                           size_t lds, hipStream_t s)
     {
-        return rows_db<D, BITS>(a, gpl, nproj, f32, multi, grid, lds, s);
+        return rows_db<D, BITS>(a, gpl, nproj, f32, units, n_cu, lds, s);
     }
 };
 
 template <int D>
-hipError_t rows_d(int bits, const RowsArgs &a, int gpl, int nproj, bool f32, bool multi,
-                         dim3 grid, size_t lds, hipStream_t s)
+hipError_t rows_d(int bits, const RowsArgs &a, int gpl, int nproj, bool f32, int64_t units,
+                  int n_cu, size_t lds, hipStream_t s)
 {
-    VQ_BITS_SWITCH(bits, RowsD<D>::template run, a, gpl, nproj, f32, multi, grid, lds, s)
+    VQ_BITS_SWITCH(bits, RowsD<D>::template run, a, gpl, nproj, f32, units, n_cu, lds, s)
 }
 
 }  // namespace vq

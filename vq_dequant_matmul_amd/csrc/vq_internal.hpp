@@ -16,6 +16,7 @@ struct TensorDev {
     const uint16_t *codebook;
     const int32_t *row_map;
     int rows, cols, d, bits, K, n_experts;
+    int64_t n_stored;
     int groups;      // cols / 64
     int wpr;         // words per stored row
     int cb_dwords;   // K * d / 2

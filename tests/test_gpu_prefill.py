@@ -1,0 +1,117 @@
+"""GPU parity of the many-token path: the grouped MFMA GEMM (one projection)
+and the routed SwiGLU FFN for prefill batches, through the C ABI, against
+the CPU oracle on the same seeded inputs.  Full-size workloads are checked on
+sampled tokens (every token's output is independent of the others)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import vq_dequant_matmul_amd as vq
+from parity import check_close, dead_rows, x_to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    oracle.build(force=False)
+    vq.load_library()
+
+
+def _dev(T):
+    return vq.VQTensor.from_host(T)
+
+
+GEMM_CASES = [
+    # d, bits, rows, cols, E, rows per expert (list), dtype, dead
+    (4, 11, 704, 2816, 4, [130, 0, 77, 193], "bf16", 0),
+    (4, 11, 2816, 704, 3, [64, 1, 150], "bf16", 0),        # 5.5 blocks per row
+    (2, 8, 1024, 4096, 3, [80, 96, 33], "bf16", 127),      # skip-zero rows
+    (4, 9, 200, 512, 2, [7, 300], "f32", 5),               # ragged rows and tiles
+    (2, 10, 96, 1024, 5, [0, 0, 40, 0, 9], "bf16", 0),
+    (8, 12, 64, 256, 2, [33, 31], "bf16", 0),
+    (4, 13, 130, 384, 2, [17, 60], "bf16", 3),
+]
+
+
+@pytest.mark.parametrize("d,bits,rows,cols,E,counts,dt,dead", GEMM_CASES)
+def test_expert_gemm_parity(d, bits, rows, cols, E, counts, dt, dead):
+    K = min(1 << bits, 8192 if d == 4 else (4096 if d == 8 else 1 << bits))
+    T = synth.make_tensor(70, d * 100 + bits, rows=rows, cols=cols, d=d, bits=bits, K=K,
+                          n_experts=E, dead_rows=dead)
+    n = sum(counts)
+    x = synth.make_x(70, 9, n, cols, dt)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    y = vq.vq_expert_gemm(_dev(T), x_to_torch(x), torch.from_numpy(offs).cuda()).cpu().numpy()
+    for e in range(E):
+        lo, hi = offs[e], offs[e + 1]
+        if lo == hi:
+            continue
+        ref = oracle.linear(T, e, x[lo:hi])
+        check_close(y[lo:hi], ref, f"gemm expert {e}")
+        dz = dead_rows(T, e)
+        assert np.all(y[lo:hi][:, dz].view(np.uint32) == 0), "dead rows must be +0.0"
+
+
+def test_expert_gemm_deterministic():
+    T = synth.make_tensor(71, 1, rows=512, cols=1024, d=4, bits=9, n_experts=2)
+    x = x_to_torch(synth.make_x(71, 2, 300, 1024, "bf16"))
+    offs = torch.tensor([0, 170, 300], dtype=torch.int32).cuda()
+    W = _dev(T)
+    a = vq.vq_expert_gemm(W, x, offs).cpu().numpy()
+    b = vq.vq_expert_gemm(W, x, offs).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def _run_moe(gate, up, down, x, ids, w):
+    y = vq.vq_moe_ffn(_dev(gate), _dev(up), _dev(down), x_to_torch(x),
+                      torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda())
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,E,k,H,I,d,bits,dead,dt", [
+    (17, 8, 2, 256, 192, 4, 9, 0, "bf16"),      # just above the decode batch limit
+    (64, 8, 3, 512, 256, 2, 8, 5, "bf16"),      # skip-zero
+    (200, 16, 4, 384, 320, 4, 11, 0, "f32"),    # fp32 activations
+    (96, 4, 4, 256, 128, 2, 10, 0, "bf16"),     # every expert routed by every token
+    (40, 64, 2, 256, 128, 8, 9, 0, "bf16"),     # mostly empty experts
+])
+def test_moe_prefill_small(T, E, k, H, I, d, bits, dead, dt):
+    seed = 80 + T
+    gate = synth.make_tensor(seed, 1, rows=I, cols=H, d=d, bits=bits, n_experts=E, dead_rows=dead)
+    up = synth.make_tensor(seed, 2, rows=I, cols=H, d=d, bits=bits, n_experts=E, dead_rows=dead)
+    down = synth.make_tensor(seed, 3, rows=H, cols=I, d=d, bits=bits, n_experts=E, dead_rows=dead)
+    x = synth.make_x(seed, 4, T, H, dt)
+    ids, w = synth.make_routes(seed, 5, T, E, k)
+    y = _run_moe(gate, up, down, x, ids, w)
+    check_close(y, oracle.moe_ffn(gate, up, down, x, ids, w), "moe prefill")
+
+
+@pytest.mark.parametrize("name,n_sample", [
+    ("moe_prefill_e128_h2816_i704_d4k2048_t2048", 6),
+    ("moe_prefill_e512_h4096_i1024_d2k256_t4096_sz", 4),
+])
+def test_moe_prefill_full_size_sampled(name, n_sample):
+    wl = synth.WORKLOADS[name]
+    gate, up, down = synth.make_moe_layer(wl)
+    x, ids, w = synth.make_moe_inputs(wl, 0)
+    y = _run_moe(gate, up, down, x, ids, w)
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(5)
+    tokens = np.sort(rng.choice(wl.n_tok, size=n_sample, replace=False)).astype(np.int32)
+    ref = oracle.moe_ffn(gate, up, down, x, ids, w, tokens=tokens)
+    check_close(y[tokens], ref, name)
+
+
+def test_moe_prefill_deterministic():
+    E, k, H, I, T = 16, 4, 512, 256, 128
+    gate = synth.make_tensor(90, 1, rows=I, cols=H, d=4, bits=9, n_experts=E)
+    up = synth.make_tensor(90, 2, rows=I, cols=H, d=4, bits=9, n_experts=E)
+    down = synth.make_tensor(90, 3, rows=H, cols=I, d=4, bits=9, n_experts=E)
+    x = synth.make_x(90, 4, T, H, "bf16")
+    ids, w = synth.make_routes(90, 5, T, E, k)
+    a = _run_moe(gate, up, down, x, ids, w)
+    b = _run_moe(gate, up, down, x, ids, w)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))

@@ -1,27 +1,448 @@
-// vq_prefill.hip -- grouped MFMA GEMM path for large token counts (gfx950).
-#include "vq_common.hpp"
-#include "vq_internal.hpp"
+// vq_prefill.hip -- routing, tiling and launch of the grouped MFMA GEMM path.
+//
+// A batch of many tokens is regrouped by expert (the routing of the model
+// cards: 10 of 512 experts on "Qwen3.8-Flash-Next-VQ-4.4bpw", top-8 of 128 on
+// "gemma-4-26b-a4b-it-VQ-6.2bpw"): counts per expert, an exclusive scan, and
+// a scatter of every (token, slot) pair to its grouped position.  The order
+// of pairs inside one expert's block is not fixed (atomic slots), but no
+// output depends on it: every output row is computed on its own and the
+// final combine sums each token's slots in slot order.
+#include <cmath>
+
+#include "vq_prefill_impl.hpp"
 
 namespace vq {
 
-size_t gemm_workspace_bytes(const TensorDev &, int) { return 0; }
+#define VQ_DECL_GEMM(N)                                                                      \
+    extern template hipError_t gemm_d<N>(int, int, int, bool, const GemmArgs &, dim3, size_t, \
+                                         hipStream_t);
+VQ_DECL_GEMM(2)
+VQ_DECL_GEMM(4)
+VQ_DECL_GEMM(8)
+#undef VQ_DECL_GEMM
 
-hipError_t launch_expert_gemm(const TensorDev &, int, const void *, int, const int32_t *, float *,
-                              void *, hipStream_t)
+constexpr int kRouteThreads = 1024;
+constexpr int kMaxRouteExperts = 4096;
+
+// Exclusive scan of v[0..n) in place (n <= 4 * kRouteThreads); returns the
+// total.  Called by all threads of the block; uses 16 + 1 ints of scratch.
+__device__ int block_exclusive_scan(int *v, int n, int *scratch)
 {
-    return hipErrorNotSupported;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    constexpr int ITEMS = 4;
+    int local[ITEMS];
+    int sum = 0;
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+        const int i = tid * ITEMS + k;
+        local[k] = (i < n) ? v[i] : 0;
+        sum += local[k];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (lane >= o)
+            incl += t;
+    }
+    if (lane == 63)
+        scratch[wave] = incl;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int w = 0; w < kRouteThreads / 64; ++w) {
+            const int t = scratch[w];
+            scratch[w] = run;
+            run += t;
+        }
+        scratch[16] = run;
+    }
+    __syncthreads();
+    int run = scratch[wave] + incl - sum;
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+        const int i = tid * ITEMS + k;
+        if (i < n)
+            v[i] = run;
+        run += local[k];
+    }
+    const int total = scratch[16];
+    __syncthreads();
+    return total;
 }
 
-size_t moe_prefill_workspace_bytes(const TensorDev &, const TensorDev &, const TensorDev &, int, int)
+// Tiles of at most mt rows per expert, rows split evenly: tiles[t] =
+// (expert, first grouped position, rows).  cnt, offs, toff: LDS arrays of E.
+__device__ void build_tiles(const int *cnt, const int *offs, int *toff, int E, int mt,
+                            int32_t *tiles, int32_t *n_tiles, int *scratch)
 {
-    return 0;
+    for (int e = threadIdx.x; e < E; e += kRouteThreads)
+        toff[e] = (cnt[e] + mt - 1) / mt;
+    __syncthreads();
+    const int total = block_exclusive_scan(toff, E, scratch);
+    for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+        const int c = cnt[e];
+        if (c == 0)
+            continue;
+        const int nt = (c + mt - 1) / mt;
+        const int per = (c + nt - 1) / nt;
+        for (int j = 0; j < nt; ++j) {
+            const int t = toff[e] + j;
+            tiles[3 * t + 0] = e;
+            tiles[3 * t + 1] = offs[e] + j * per;
+            tiles[3 * t + 2] = min(per, c - j * per);
+        }
+    }
+    if (threadIdx.x == 0)
+        *n_tiles = total;
 }
 
-hipError_t launch_moe_prefill(const TensorDev &, const TensorDev &, const TensorDev &, int, int,
-                              const void *, int, const int32_t *, const float *, float *, void *,
-                              hipStream_t)
+// Route grouping for the MoE FFN: pairs q = t*top_k + s by expert.
+__global__ __launch_bounds__(kRouteThreads) void k_route(const int32_t *__restrict__ ids, int P,
+                                                         int E, int mt, int32_t *__restrict__ offs,
+                                                         int32_t *__restrict__ perm,
+                                                         int32_t *__restrict__ pos,
+                                                         int32_t *__restrict__ tiles,
+                                                         int32_t *__restrict__ n_tiles,
+                                                         uint32_t *__restrict__ zero_buf,
+                                                         int zero_n)
 {
-    return hipErrorNotSupported;
+    extern __shared__ int s[];
+    int *cnt = s, *base = s + E, *fill = s + 2 * E, *toff = s + 3 * E, *scratch = s + 4 * E;
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += kRouteThreads) {
+        cnt[e] = 0;
+        fill[e] = 0;
+    }
+    for (int i = tid; i < zero_n; i += kRouteThreads)
+        zero_buf[i] = 0u;
+    __syncthreads();
+    for (int q = tid; q < P; q += kRouteThreads)
+        atomicAdd(&cnt[ids[q]], 1);
+    __syncthreads();
+    for (int e = tid; e < E; e += kRouteThreads)
+        base[e] = cnt[e];
+    __syncthreads();
+    const int total = block_exclusive_scan(base, E, scratch);
+    for (int e = tid; e < E; e += kRouteThreads)
+        offs[e] = base[e];
+    if (tid == 0)
+        offs[E] = total;
+    for (int q = tid; q < P; q += kRouteThreads) {
+        const int e = ids[q];
+        const int p = base[e] + atomicAdd(&fill[e], 1);
+        perm[p] = q;
+        pos[q] = p;
+    }
+    __syncthreads();
+    build_tiles(cnt, base, toff, E, mt, tiles, n_tiles, scratch);
+}
+
+// Tiles for a grouped GEMM whose rows are already grouped by expert.
+__global__ __launch_bounds__(kRouteThreads) void k_tiles_from_offsets(
+    const int32_t *__restrict__ expert_offsets, int E, int mt, int32_t *__restrict__ tiles,
+    int32_t *__restrict__ n_tiles)
+{
+    extern __shared__ int s[];
+    int *cnt = s, *base = s + E, *toff = s + 2 * E, *scratch = s + 3 * E;
+    for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+        base[e] = expert_offsets[e];
+        cnt[e] = max(0, expert_offsets[e + 1] - expert_offsets[e]);
+    }
+    __syncthreads();
+    build_tiles(cnt, base, toff, E, mt, tiles, n_tiles, scratch);
+}
+
+// Bits of max |x| of each row (non-negative floats order like their bits).
+__global__ __launch_bounds__(256) void k_rowmax(const void *__restrict__ x, int f32, int rows,
+                                                int cols, int64_t stride,
+                                                uint32_t *__restrict__ out)
+{
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= rows)
+        return;
+    uint32_t mx = 0;
+    if (f32) {
+        const float *p = static_cast<const float *>(x) + (int64_t)row * stride;
+        for (int c = lane * 4; c < cols; c += 256) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(p + c);
+            mx = max(mx, max(max(q.x & 0x7fffffffu, q.y & 0x7fffffffu),
+                             max(q.z & 0x7fffffffu, q.w & 0x7fffffffu)));
+        }
+    } else {
+        const uint16_t *p = static_cast<const uint16_t *>(x) + (int64_t)row * stride;
+        for (int c = lane * 8; c < cols; c += 512) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(p + c);
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                mx = max(mx, max((w[k] & 0x7fffu) << 16, (w[k] >> 16 & 0x7fffu) << 16));
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1)
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+    if (lane == 0)
+        out[row] = mx;
+}
+
+// y[t][c] = sum over slots s (in order) of w[t][s] * z[pos[t*k+s]][c]
+__global__ __launch_bounds__(256) void k_combine_perm(const float *__restrict__ z,
+                                                      const int32_t *__restrict__ pos,
+                                                      const float *__restrict__ w, int n_tok,
+                                                      int top_k, int hidden, float *__restrict__ y)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t n4 = (int64_t)n_tok * hidden / 4;
+    if (i >= n4)
+        return;
+    const int64_t t = (i * 4) / hidden;
+    const int64_t c = (i * 4) % hidden;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+    for (int s = 0; s < top_k; ++s) {
+        const float ws = w[t * top_k + s];
+        const float4 v =
+            *reinterpret_cast<const float4 *>(z + (int64_t)pos[t * top_k + s] * hidden + c);
+        acc.x += ws * v.x;
+        acc.y += ws * v.y;
+        acc.z += ws * v.z;
+        acc.w += ws * v.w;
+    }
+    *reinterpret_cast<float4 *>(y + t * hidden + c) = acc;
+}
+
+// Zero fill (used when every row of a tensor is dead: the product is zero).
+__global__ __launch_bounds__(256) void k_zero(float *__restrict__ p, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n)
+        p[i] = 0.0f;
+}
+
+// --------------------------------------------------------------------------------
+// host side
+// --------------------------------------------------------------------------------
+
+static hipError_t launch_zero(float *p, int64_t n, hipStream_t stream)
+{
+    if (n <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
+
+static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Tile height: 192 rows when the expected largest expert block (mean + 4
+// standard deviations of a binomial count) exceeds 128, else 128.
+static int pick_mb(int64_t rows, int E)
+{
+    const double mean = (double)rows / E;
+    return (mean + 4.0 * sqrt(mean) > 128.0) ? 6 : 4;
+}
+
+static int64_t max_tiles(int64_t rows, int E, int mt)
+{
+    return rows / mt + (rows < E ? rows : E) + 1;
+}
+
+static size_t gemm_lds_bytes(const TensorDev &t0, const TensorDev *t1, int mb, int &cb_offset1,
+                             int &a_offset)
+{
+    cb_offset1 = (t0.cb_dwords + 3) & ~3;
+    int off = t1 ? cb_offset1 + t1->cb_dwords : t0.cb_dwords;
+    off = (off + 3) & ~3;
+    a_offset = off;
+    off += 2 * 32 * mb * kAStride / 2;
+    return (size_t)off * 4;
+}
+
+static hipError_t launch_gemm(const TensorDev &t0, const TensorDev *t1, int mb, const void *act,
+                              bool act_f32, int64_t act_stride, const int32_t *perm, int act_div,
+                              const uint32_t *amax, const int32_t *tiles, const int32_t *n_tiles,
+                              int64_t tiles_cap, float *out, int64_t out_stride,
+                              uint32_t *out_amax, hipStream_t stream)
+{
+    GemmArgs a = {};
+    const TensorDev *ts[2] = {&t0, t1};
+    const int nproj = t1 ? 2 : 1;
+    for (int p = 0; p < nproj; ++p) {
+        a.codes[p] = ts[p]->codes;
+        a.scales[p] = ts[p]->scales;
+        a.row_map[p] = ts[p]->row_map;
+        a.codebook[p] = ts[p]->codebook;
+        a.cb_dwords[p] = ts[p]->cb_dwords;
+    }
+    const size_t lds = gemm_lds_bytes(t0, t1, mb, a.cb_offset1, a.a_offset);
+    a.rows = t0.rows;
+    a.cols = t0.cols;
+    a.groups = t0.groups;
+    a.wpr = t0.wpr;
+    a.act = act;
+    a.act_stride = act_stride;
+    a.perm = perm;
+    a.act_div = act_div > 0 ? act_div : 1;
+    a.amax = amax;
+    a.tiles = tiles;
+    a.n_tiles = n_tiles;
+    a.out = out;
+    a.out_stride = out_stride;
+    a.out_amax = out_amax;
+    if (tiles_cap > 65535)
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((t0.rows + kGemmN - 1) / kGemmN), (unsigned)tiles_cap);
+    switch (t0.d) {
+    case 2: return gemm_d<2>(t0.bits, nproj, mb, act_f32, a, grid, lds, stream);
+    case 4: return gemm_d<4>(t0.bits, nproj, mb, act_f32, a, grid, lds, stream);
+    case 8: return gemm_d<8>(t0.bits, nproj, mb, act_f32, a, grid, lds, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// ---- vq_expert_gemm ------------------------------------------------------------
+
+struct GemmWs {
+    size_t tiles, n_tiles, amax, total;
+    int mb;
+    int64_t cap;
+};
+
+static GemmWs gemm_ws(const TensorDev &t, int n_x_rows)
+{
+    GemmWs w;
+    w.mb = pick_mb(n_x_rows, t.n_experts);
+    w.cap = max_tiles(n_x_rows, t.n_experts, 32 * w.mb);
+    w.tiles = 0;
+    w.n_tiles = align256(w.tiles + (size_t)w.cap * 3 * 4);
+    w.amax = align256(w.n_tiles + 4);
+    w.total = align256(w.amax + (size_t)n_x_rows * 4);
+    return w;
+}
+
+size_t gemm_workspace_bytes(const TensorDev &t, int n_x_rows)
+{
+    return gemm_ws(t, n_x_rows).total;
+}
+
+hipError_t launch_expert_gemm(const TensorDev &t, int n_x_rows, const void *x, int x_f32,
+                              const int32_t *expert_offsets, float *y, void *ws,
+                              hipStream_t stream)
+{
+    if (t.n_experts > kMaxRouteExperts)
+        return hipErrorNotSupported;
+    const GemmWs w = gemm_ws(t, n_x_rows);
+    char *base = static_cast<char *>(ws);
+    int32_t *tiles = reinterpret_cast<int32_t *>(base + w.tiles);
+    int32_t *n_tiles = reinterpret_cast<int32_t *>(base + w.n_tiles);
+    uint32_t *amax = reinterpret_cast<uint32_t *>(base + w.amax);
+    const size_t lds_t = (size_t)(3 * t.n_experts + 17) * 4;
+    hipLaunchKernelGGL(k_tiles_from_offsets, dim3(1), dim3(kRouteThreads), lds_t, stream,
+                       expert_offsets, t.n_experts, 32 * w.mb, tiles, n_tiles);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_rowmax, dim3((unsigned)((n_x_rows + 3) / 4)), dim3(256), 0, stream, x,
+                       x_f32, n_x_rows, t.cols, (int64_t)t.cols, amax);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    if (t.n_stored == 0) {
+        // every row dead: the product is exactly zero
+        return launch_zero(y, (int64_t)n_x_rows * t.rows, stream);
+    }
+    return launch_gemm(t, nullptr, w.mb, x, x_f32 != 0, t.cols, nullptr, 1, amax, tiles, n_tiles,
+                       w.cap, y, t.rows, nullptr, stream);
+}
+
+// ---- vq_moe_ffn, many tokens ---------------------------------------------------
+
+struct FfnWs {
+    size_t offs, perm, pos, tiles, n_tiles, xmax, hmax, h, z, total;
+    int mb;
+    int64_t cap;
+};
+
+static FfnWs ffn_ws(const TensorDev &g, const TensorDev &dn, int n_tok, int top_k)
+{
+    FfnWs w;
+    const int64_t P = (int64_t)n_tok * top_k;
+    w.mb = pick_mb(P, g.n_experts);
+    w.cap = max_tiles(P, g.n_experts, 32 * w.mb);
+    size_t o = 0;
+    w.offs = o;
+    o = align256(o + (size_t)(g.n_experts + 1) * 4);
+    w.perm = o;
+    o = align256(o + (size_t)P * 4);
+    w.pos = o;
+    o = align256(o + (size_t)P * 4);
+    w.tiles = o;
+    o = align256(o + (size_t)w.cap * 12);
+    w.n_tiles = o;
+    o = align256(o + 4);
+    w.xmax = o;
+    o = align256(o + (size_t)n_tok * 4);
+    w.hmax = o;
+    o = align256(o + (size_t)P * 4);
+    w.h = o;
+    o = align256(o + (size_t)P * g.rows * 4);
+    w.z = o;
+    o = align256(o + (size_t)P * dn.rows * 4);
+    w.total = o;
+    return w;
+}
+
+size_t moe_prefill_workspace_bytes(const TensorDev &g, const TensorDev &, const TensorDev &dn,
+                                   int n_tok, int top_k)
+{
+    return ffn_ws(g, dn, n_tok, top_k).total;
+}
+
+hipError_t launch_moe_prefill(const TensorDev &g, const TensorDev &u, const TensorDev &dn,
+                              int n_tok, int top_k, const void *x, int x_f32, const int32_t *ids,
+                              const float *wts, float *y, void *ws, hipStream_t stream)
+{
+    if (g.n_experts > kMaxRouteExperts)
+        return hipErrorNotSupported;
+    const FfnWs w = ffn_ws(g, dn, n_tok, top_k);
+    char *base = static_cast<char *>(ws);
+    int32_t *offs = reinterpret_cast<int32_t *>(base + w.offs);
+    int32_t *perm = reinterpret_cast<int32_t *>(base + w.perm);
+    int32_t *pos = reinterpret_cast<int32_t *>(base + w.pos);
+    int32_t *tiles = reinterpret_cast<int32_t *>(base + w.tiles);
+    int32_t *n_tiles = reinterpret_cast<int32_t *>(base + w.n_tiles);
+    uint32_t *xmax = reinterpret_cast<uint32_t *>(base + w.xmax);
+    uint32_t *hmax = reinterpret_cast<uint32_t *>(base + w.hmax);
+    float *h = reinterpret_cast<float *>(base + w.h);
+    float *z = reinterpret_cast<float *>(base + w.z);
+    const int P = n_tok * top_k;
+    const int E = g.n_experts;
+
+    const size_t lds_r = (size_t)(4 * E + 17) * 4;
+    hipLaunchKernelGGL(k_route, dim3(1), dim3(kRouteThreads), lds_r, stream, ids, P, E,
+                       32 * w.mb, offs, perm, pos, tiles, n_tiles, hmax, P);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_rowmax, dim3((unsigned)((n_tok + 3) / 4)), dim3(256), 0, stream, x,
+                       x_f32, n_tok, g.cols, (int64_t)g.cols, xmax);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    if (g.n_stored == 0 || u.n_stored == 0 || dn.n_stored == 0)
+        return launch_zero(y, (int64_t)n_tok * dn.rows, stream);
+    e = launch_gemm(g, &u, w.mb, x, x_f32 != 0, g.cols, perm, top_k, xmax, tiles, n_tiles, w.cap,
+                    h, g.rows, hmax, stream);
+    if (e != hipSuccess)
+        return e;
+    e = launch_gemm(dn, nullptr, w.mb, h, true, g.rows, nullptr, 1, hmax, tiles, n_tiles, w.cap, z,
+                    dn.rows, nullptr, stream);
+    if (e != hipSuccess)
+        return e;
+    const int64_t n4 = (int64_t)n_tok * dn.rows / 4;
+    hipLaunchKernelGGL(k_combine_perm, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, z,
+                       pos, wts, n_tok, top_k, dn.rows, y);
+    return hipGetLastError();
 }
 
 }  // namespace vq

@@ -1,0 +1,8 @@
+// vq_prefill_d2.hip -- grouped MFMA GEMM instantiations for d = 2.
+#include "vq_prefill_impl.hpp"
+
+namespace vq {
+
+template hipError_t gemm_d<2>(int, int, int, bool, const GemmArgs &, dim3, size_t, hipStream_t);
+
+}  // namespace vq

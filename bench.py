@@ -2,28 +2,34 @@
 """Benchmark of the VQ MoE expert matmul on one MI355X.
 
 A step is one pass of the routed SwiGLU expert FFN (``vq_moe_ffn``: route
-grouping, codebook staging, code unpacking, lookup-and-scale, the fused
-dot products, SwiGLU, the down projection and the gate-weighted combine)
-over one batch of synthetic input.  The default workload is the decode step
-of a 128-expert, top-8 layer (hidden 2048, expert inter 768) with every
-projection at d=4/K=512 (9-bit codes), one token per step.
+grouping, codebook staging, code unpacking, lookup-and-scale, the fused dot
+products or MFMA tiles, SwiGLU, the down projection and the gate-weighted
+combine) over one batch of synthetic input.  The default workload is the
+decode step of a 128-expert, top-8 layer (hidden 2048, expert inter 768)
+with every projection at d=4/K=512 (9-bit codes), one token per step;
+``--workload`` selects the other seeded layers (decode batches of 1 and 8
+tokens on a 512-expert top-10 layer; prefill of 2048 / 4096 tokens).
 
 Inputs are resident in HBM before timing starts.  Each step uses fresh
 routes and activations, and steps rotate over several copies of the layer at
-distinct addresses so the weights come from HBM, not from the 256 MB
-Infinity Cache.  The K timed steps are captured once in a HIP graph and
-replayed (the launches are the only thing a graph removes; every kernel runs).
-``value`` is algorithmic bytes / wall time: the routed experts' packed codes,
-scales and row maps, the codebooks, activations, outputs, ids and weights.
+distinct addresses so the weights come from HBM, not the 256 MB Infinity
+Cache.  The K timed steps are captured once in a HIP graph and replayed
+(a graph removes launch overhead only; every kernel runs).
 
-The JSON line also carries ``roofline`` for the dominant kernel (the fused
-gate+up+SwiGLU launch, timed per launch with HIP events on its stream) and
-``cpu_baseline`` (the CPU oracle timed on a bounded sample of the same
-workload on the host's cores).
+Decode workloads report GB/s of algorithmic bytes (the routed experts'
+packed codes, scales and row maps, the codebooks, activations, outputs, ids
+and weights) against the 8 TB/s HBM peak; prefill workloads report TFLOP/s
+of algorithmic flops (2 x live weight rows x columns per routed pair, over
+the three projections) against the 2.5 PFLOP/s dense fp16 MFMA peak.
+
+``roofline`` times the dominant kernel (the fused gate+up launch) per
+launch with HIP events recorded on its own stream; ``cpu_baseline`` times
+the CPU oracle on a bounded sample of the same workload on the host cores.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -35,10 +41,12 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "VQ MoE expert GB/s (decode, % HBM peak) and TFLOP/s (prefill, % MFMA peak)"
-HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
-MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 MALL_BYTES = 256 << 20
 DEFAULT_WORKLOAD = "moe_decode_e128_h2048_i768_d4k512_b1"
+CSRC = os.path.join(ROOT, "vq_dequant_matmul_amd", "csrc")
+TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def log(*a):
@@ -48,16 +56,68 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=None, help="timed steps (default 200 decode, 20 prefill)")
+    p.add_argument("--warmup", type=int, default=None, help="untimed steps (default 20 / 3)")
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--layers", type=int, default=0, help="layer copies (0 = auto)")
     p.add_argument("--no-graph", action="store_true", help="time eager launches")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="target CPU time of the oracle baseline sample (0 = skip)")
-    p.add_argument("--kernel-launches", type=int, default=100,
+    p.add_argument("--kernel-launches", type=int, default=None,
                    help="launches of the dominant kernel timed with HIP events")
     return p.parse_args()
+
+
+class HipEvents:
+    """hipEventCreate / hipEventElapsedTime through the HIP runtime."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, ev):
+        self.hip.hipEventDestroy(ev)
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources; recorded counter traffic is valid only for it."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the recorded
+    rocprofv3 FETCH_SIZE / WRITE_SIZE runs (calibrated against a copy of known
+    size), or None when none was recorded for the current kernel sources."""
+    try:
+        with open(TRAFFIC) as f:
+            rec = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash():
+        return None
+    return int(rec["bytes_per_launch"])
 
 
 def expert_bytes(T, e: int) -> int:
@@ -90,11 +150,10 @@ def main():
     vq.load_library()
 
     wl = synth.WORKLOADS[args.workload]
-    if wl.n_tok > 16:
-        print(f"{args.workload}: prefill workloads are timed by the grouped-GEMM path",
-              file=sys.stderr)
-        sys.exit(2)
-    K, W = args.steps, args.warmup
+    prefill = wl.n_tok > 16
+    K = args.steps if args.steps is not None else (20 if prefill else 200)
+    W = args.warmup if args.warmup is not None else (3 if prefill else 20)
+    n_k = args.kernel_launches if args.kernel_launches is not None else (10 if prefill else 100)
     n_steps = K + W
 
     # ---- layer, copies, per-step inputs (all resident before timing) ---------------
@@ -118,10 +177,14 @@ def main():
     workspace = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     log(f"[bench] {args.workload}: {L} layer copies x {layer_bytes / 1e6:.1f} MB, "
-        f"{n_steps} step inputs, setup {time.perf_counter() - t0:.1f}s")
+        f"{n_steps} step inputs, workspace {ws_bytes / 1e6:.1f} MB, "
+        f"setup {time.perf_counter() - t0:.1f}s")
 
+    # ---- algorithmic work -------------------------------------------------------------
     cb_bytes = sum(t.K * t.d * 2 for t in (gate_h, up_h, down_h))
     io_bytes = wl.n_tok * wl.hidden * (2 + 4) + wl.n_tok * wl.top_k * 8
+    live = {id(t): np.array([t.expert_stored_rows(e) for e in range(wl.n_experts)])
+            for t in (gate_h, up_h, down_h)}
 
     def step_bytes(i):
         uniq = np.unique(ids[i])
@@ -133,6 +196,14 @@ def main():
         return int(sum(expert_bytes(t, int(e)) for e in uniq for t in (gate_h, up_h))
                    + gate_h.K * gate_h.d * 2 + up_h.K * up_h.d * 2
                    + wl.n_tok * wl.hidden * 2 + wl.n_tok * wl.top_k * (4 + 4 * wl.inter))
+
+    def gate_up_flops(i):
+        r = ids[i].ravel()
+        return int(2 * wl.hidden * (live[id(gate_h)][r].sum() + live[id(up_h)][r].sum()))
+
+    def step_flops(i):
+        r = ids[i].ravel()
+        return gate_up_flops(i) + int(2 * wl.inter * live[id(down_h)][r].sum())
 
     def step(i):
         G, U, D = layers[i % L]
@@ -173,38 +244,56 @@ def main():
     if not graph_check:
         log("[bench] WARNING: graph replay differs from eager")
 
-    total_bytes = sum(step_bytes(i) for i in range(W, n_steps))
-    value = total_bytes / elapsed / 1e9
+    if prefill:
+        total = sum(step_flops(i) for i in range(W, n_steps))
+        value, unit = total / elapsed / 1e12, "TFLOP/s"
+        frac = value / MFMA_F16_PEAK_TFLOPS
+    else:
+        total = sum(step_bytes(i) for i in range(W, n_steps))
+        value, unit = total / elapsed / 1e9, "GB/s"
+        frac = value / HBM_PEAK_GBS
     ms_per_step = elapsed * 1e3 / K
 
-    # ---- dominant kernel: fused gate+up+SwiGLU, per-launch HIP events -------------------
-    n_k = max(1, args.kernel_launches)
-    h_buf = torch.empty((wl.n_tok * wl.top_k, wl.inter), dtype=torch.float32, device="cuda")
-    backlog = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_k)]
+    # ---- dominant kernel: fused gate+up launch, HIP events on its stream -------------
+    hip = HipEvents()
+    pairs = [(hip.create(), hip.create()) for _ in range(n_k)]
+    # A queue of 256 MiB device copies keeps the GPU busy while the launches
+    # are queued (the events then bracket back-to-back kernels); the copy is
+    # also the kernel of known size the HBM byte counters are calibrated on.
+    src = torch.ones(1 << 26, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    for _ in range(48):           # keep the GPU busy while the launches are queued
-        backlog.fill_(1.0)
+    for _ in range(48):
+        dst.copy_(src)
     for j in range(n_k):
-        i = W + (j % K)
-        G, U, _ = layers[i % L]
-        evs[j][0].record()
-        vq.vq_moe_gate_up(G, U, x_dev[i], ids_dev[i], out=h_buf)
-        evs[j][1].record()
+        vq.vq_set_kernel_events(pairs[j][0], pairs[j][1])
+        step(W + (j % K))
+    vq.vq_set_kernel_events(None, None)
     torch.cuda.synchronize()
-    durs = np.array([a.elapsed_time(b) * 1e-3 for a, b in evs])       # seconds
-    kbytes = np.array([gate_up_bytes(W + (j % K)) for j in range(n_k)])
+    durs = np.array([hip.elapsed_ms(a, b) * 1e-3 for a, b in pairs])     # seconds
+    for a, b in pairs:
+        hip.destroy(a)
+        hip.destroy(b)
+    del src, dst
     k_mean = float(durs.mean())
-    achieved = float(kbytes.mean() / k_mean / 1e9)
-    del backlog
-    roofline = {
-        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-        "kernel": "vq::k_rows (gate+up+SwiGLU, fused)",
-        "launch_us": round(k_mean * 1e6, 2), "bytes_per_launch": int(kbytes.mean()),
-    }
-    log(f"[bench] dominant kernel: {k_mean * 1e6:.2f} us/launch, {achieved:.0f} GB/s")
+    if prefill:
+        kwork = np.array([gate_up_flops(W + (j % K)) for j in range(n_k)])
+        achieved = float(kwork.mean() / k_mean / 1e12)
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1),
+                    "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
+                    "traffic": recorded_traffic(args.workload),
+                    "kernel": "vq::k_gemm (gate+up grouped GEMM, SwiGLU epilogue)",
+                    "launch_us": round(k_mean * 1e6, 2), "flops_per_launch": int(kwork.mean())}
+    else:
+        kwork = np.array([gate_up_bytes(W + (j % K)) for j in range(n_k)])
+        achieved = float(kwork.mean() / k_mean / 1e9)
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": recorded_traffic(args.workload),
+                    "kernel": "vq::k_rows (gate+up+SwiGLU, fused)",
+                    "launch_us": round(k_mean * 1e6, 2), "bytes_per_launch": int(kwork.mean())}
+    log(f"[bench] dominant kernel: {k_mean * 1e6:.2f} us/launch, {achieved:.1f} {roofline['unit']}")
 
     # ---- CPU oracle on a bounded sample ------------------------------------------------
     cpu = None
@@ -212,32 +301,49 @@ def main():
         import oracle
         oracle.build(force=False)
         cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-        t_cpu, n_cpu, b_cpu = 0.0, 0, 0
+        t_cpu, n_cpu, work = 0.0, 0, 0
+        rng = np.random.default_rng(0)
         while t_cpu < args.cpu_seconds and n_cpu < n_steps:
             i = W + n_cpu % K
-            c0 = time.perf_counter()
-            oracle.moe_ffn(gate_h, up_h, down_h, xs[i], ids[i], ws[i])
-            t_cpu += time.perf_counter() - c0
-            b_cpu += step_bytes(i)
+            if prefill:
+                # a few tokens of the step: each token's output is independent
+                toks = np.sort(rng.choice(wl.n_tok, size=2, replace=False)).astype(np.int32)
+                c0 = time.perf_counter()
+                oracle.moe_ffn(gate_h, up_h, down_h, xs[i], ids[i], ws[i], tokens=toks)
+                t_cpu += time.perf_counter() - c0
+                r = ids[i][toks].ravel()
+                work += int(2 * wl.hidden * (live[id(gate_h)][r].sum() + live[id(up_h)][r].sum())
+                            + 2 * wl.inter * live[id(down_h)][r].sum())
+            else:
+                c0 = time.perf_counter()
+                oracle.moe_ffn(gate_h, up_h, down_h, xs[i], ids[i], ws[i])
+                t_cpu += time.perf_counter() - c0
+                work += step_bytes(i)
             n_cpu += 1
-        cpu = {"value": round(b_cpu / t_cpu / 1e9, 4), "unit": "GB/s", "cores": cores,
-               "kind": "oracle",
-               "sample": f"{n_cpu} decode steps of the same workload ({wl.n_tok} token, "
-                         f"{wl.top_k} routed experts each), {t_cpu:.1f}s"}
-        log(f"[bench] cpu oracle: {n_cpu} steps in {t_cpu:.1f}s")
+        if prefill:
+            cpu = {"value": round(work / t_cpu / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+                   "kind": "oracle",
+                   "sample": f"{n_cpu} x 2 sampled tokens of the same workload "
+                             f"({wl.top_k} routed experts each), {t_cpu:.1f}s"}
+        else:
+            cpu = {"value": round(work / t_cpu / 1e9, 4), "unit": "GB/s", "cores": cores,
+                   "kind": "oracle",
+                   "sample": f"{n_cpu} decode steps of the same workload ({wl.n_tok} token(s), "
+                             f"{wl.top_k} routed experts each), {t_cpu:.1f}s"}
+        log(f"[bench] cpu oracle: {n_cpu} samples in {t_cpu:.1f}s")
 
     rec = {
-        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": K,
         "warmup": W, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16xf16->f32",
         "data": "synthetic",
         "config": {
             "workload": args.workload, "experts": wl.n_experts, "top_k": wl.top_k,
             "hidden": wl.hidden, "inter": wl.inter, "d": wl.d, "bits": wl.bits,
-            "K": 1 << wl.bits, "tokens": wl.n_tok, "layer_copies": L,
-            "hip_graph": use_graph, "graph_replay_bit_equal": graph_check,
-            "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-            "bytes_per_step": int(total_bytes / K),
+            "K": 1 << wl.bits, "tokens": wl.n_tok, "dead_row_fraction": wl.dead_frac,
+            "layer_copies": L, "hip_graph": use_graph, "graph_replay_bit_equal": graph_check,
+            "peak_frac": round(frac, 4),
+            ("flops_per_step" if prefill else "bytes_per_step"): int(total / K),
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -169,6 +169,16 @@ vq_status vq_moe_down(const vq_tensor *down, int32_t n_tokens, int32_t top_k, co
 vq_status vq_moe_combine(int32_t n_tokens, int32_t top_k, int32_t hidden, const float *z,
                          const float *topk_weights, float *y, void *stream);
 
+/* ---- measurement -------------------------------------------------------------- */
+
+/* Until cleared (NULL, NULL), every vq_moe_ffn / vq_moe_gate_up /
+   vq_expert_gemm call made on this thread records `start` (a hipEvent_t)
+   on its stream right before its dominant kernel (the fused gate+up launch;
+   the GEMM for vq_expert_gemm) and `stop` right after it, so a caller can
+   time that one kernel with hipEventElapsedTime.  The events are owned by
+   the caller. */
+vq_status vq_set_kernel_events(void *start, void *stop);
+
 #ifdef __cplusplus
 }
 #endif

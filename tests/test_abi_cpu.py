@@ -121,3 +121,9 @@ def test_binding_refuses_without_gpu():
         pytest.skip("a GPU is visible")
     with pytest.raises(RuntimeError, match="GPU"):
         vq._require_gpu()
+
+
+def test_kernel_events_arguments(lib):
+    assert lib.vq_set_kernel_events(None, None) == 0
+    st = lib.vq_set_kernel_events(FAKE, None)
+    assert st == 1 and "both" in lib.vq_last_error().decode()

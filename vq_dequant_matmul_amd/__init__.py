@@ -75,6 +75,7 @@ def load_library():
         "vq_moe_gate_up": (ctypes.c_int, [T, T, I32, I32, P, ctypes.c_int, P, P, P]),
         "vq_moe_down": (ctypes.c_int, [T, I32, I32, P, P, P, P]),
         "vq_moe_combine": (ctypes.c_int, [I32, I32, I32, P, P, P, P]),
+        "vq_set_kernel_events": (ctypes.c_int, [P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -307,9 +308,16 @@ def vq_moe_combine(z: torch.Tensor, topk_weights: torch.Tensor,
     return out
 
 
+def vq_set_kernel_events(start, stop) -> None:
+    """Record HIP events `start` / `stop` (raw hipEvent_t handles, or None to
+    clear) around the dominant kernel of the following calls on this thread."""
+    _check(load_library().vq_set_kernel_events(start, stop))
+
+
 __all__ = [
     "VQError", "VQTensor", "build", "load_library", "vq_validate", "vq_dequantize",
     "vq_expert_gemv", "vq_expert_gemm", "vq_expert_gemm_workspace_size", "vq_moe_ffn",
     "vq_moe_ffn_workspace_size", "vq_moe_gate_up", "vq_moe_down", "vq_moe_combine",
+    "vq_set_kernel_events",
     "VQ_F32", "VQ_BF16",
 ]

@@ -128,6 +128,12 @@ constexpr int kGemvMaxTokens = 64;
 
 namespace vq {
 
+KernelEvents &kernel_events()
+{
+    thread_local KernelEvents ev = {nullptr, nullptr};
+    return ev;
+}
+
 TensorDev to_dev(const vq_tensor &t)
 {
     TensorDev d;
@@ -169,6 +175,15 @@ VQ_EXPORT const char *vq_status_string(vq_status s)
 }
 
 VQ_EXPORT const char *vq_last_error(void) { return g_last_error.c_str(); }
+
+VQ_EXPORT vq_status vq_set_kernel_events(void *start, void *stop)
+{
+    if ((start == nullptr) != (stop == nullptr))
+        return fail(VQ_ERR_INVALID_ARGUMENT, "start and stop must both be set or both be NULL");
+    vq::kernel_events().start = static_cast<hipEvent_t>(start);
+    vq::kernel_events().stop = static_cast<hipEvent_t>(stop);
+    return ok();
+}
 
 VQ_EXPORT vq_status vq_validate(const vq_tensor *W)
 {
@@ -313,7 +328,13 @@ static hipError_t launch_gate_up(const vq::TensorDev &g, const vq::TensorDev &u,
     L.n_slots = n_tokens * top_k;
     L.act_div = top_k;
     L.multi_per_expert = n_tokens > 1;
-    return vq::launch_rows(L, s);
+    const vq::KernelEvents &ev = vq::kernel_events();
+    if (ev.start)
+        (void)hipEventRecord(ev.start, s);
+    const hipError_t e = vq::launch_rows(L, s);
+    if (ev.stop)
+        (void)hipEventRecord(ev.stop, s);
+    return e;
 }
 
 static hipError_t launch_down(const vq::TensorDev &dn, int n_tokens, int top_k, const float *h,

@@ -68,6 +68,13 @@ hipError_t launch_moe_prefill(const TensorDev &g, const TensorDev &u, const Tens
                               const int32_t *ids, const float *w, float *y, void *ws,
                               hipStream_t stream);
 
+// Events the caller asked to record around the dominant kernel of the next
+// calls on this thread (both null = off).
+struct KernelEvents {
+    hipEvent_t start, stop;
+};
+KernelEvents &kernel_events();
+
 // Limits of the decode engine.
 constexpr int kMaxSlots = 1024;      // n_tokens * top_k in one routed launch
 constexpr int kMaxGroupsDecode = 128; // cols <= 8192

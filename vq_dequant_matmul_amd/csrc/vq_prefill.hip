@@ -352,8 +352,14 @@ hipError_t launch_expert_gemm(const TensorDev &t, int n_x_rows, const void *x, i
         // every row dead: the product is exactly zero
         return launch_zero(y, (int64_t)n_x_rows * t.rows, stream);
     }
-    return launch_gemm(t, nullptr, w.mb, x, x_f32 != 0, t.cols, nullptr, 1, amax, tiles, n_tiles,
-                       w.cap, y, t.rows, nullptr, stream);
+    const KernelEvents &ev = kernel_events();
+    if (ev.start)
+        (void)hipEventRecord(ev.start, stream);
+    e = launch_gemm(t, nullptr, w.mb, x, x_f32 != 0, t.cols, nullptr, 1, amax, tiles, n_tiles,
+                    w.cap, y, t.rows, nullptr, stream);
+    if (ev.stop)
+        (void)hipEventRecord(ev.stop, stream);
+    return e;
 }
 
 // ---- vq_moe_ffn, many tokens ---------------------------------------------------
@@ -431,8 +437,13 @@ hipError_t launch_moe_prefill(const TensorDev &g, const TensorDev &u, const Tens
         return e;
     if (g.n_stored == 0 || u.n_stored == 0 || dn.n_stored == 0)
         return launch_zero(y, (int64_t)n_tok * dn.rows, stream);
+    const KernelEvents &ev = kernel_events();
+    if (ev.start)
+        (void)hipEventRecord(ev.start, stream);
     e = launch_gemm(g, &u, w.mb, x, x_f32 != 0, g.cols, perm, top_k, xmax, tiles, n_tiles, w.cap,
                     h, g.rows, hmax, stream);
+    if (ev.stop)
+        (void)hipEventRecord(ev.stop, stream);
     if (e != hipSuccess)
         return e;
     e = launch_gemm(dn, nullptr, w.mb, h, true, g.rows, nullptr, 1, hmax, tiles, n_tiles, w.cap, z,

@@ -46,7 +46,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 MALL_BYTES = 256 << 20
 DEFAULT_WORKLOAD = "moe_decode_e128_h2048_i768_d4k512_b1"
 CSRC = os.path.join(ROOT, "vq_dequant_matmul_amd", "csrc")
-TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
 
 def log(*a):
@@ -77,6 +77,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
                                                  ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self):
         ev = ctypes.c_void_p()
@@ -84,6 +85,11 @@ class HipEvents:
         if rc != 0:
             raise RuntimeError(f"hipEventCreate failed ({rc})")
         return ev
+
+    def record(self, ev, stream):
+        rc = self.hip.hipEventRecord(ev, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def elapsed_ms(self, a, b) -> float:
         ms = ctypes.c_float()
@@ -96,28 +102,34 @@ class HipEvents:
         self.hip.hipEventDestroy(ev)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the HIP sources; recorded counter traffic is valid only for it."""
+def kernel_source_hash(family: str) -> str:
+    """Hash of the sources that build one kernel family ("decode" or
+    "prefill"); recorded counter traffic is valid only for that hash."""
     import hashlib
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        if name.startswith("vq_" + family) or name in ("vq_common.hpp", "vq_internal.hpp",
+                                                       "vq_api.cpp"):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload: str):
+def recorded_traffic(workload: str, family: str):
     """HBM bytes per launch of the dominant kernel from the recorded
-    rocprofv3 FETCH_SIZE / WRITE_SIZE runs (calibrated against a copy of known
-    size), or None when none was recorded for the current kernel sources."""
+    rocprofv3 FETCH_SIZE / WRITE_SIZE passes (each scaled by what the counter
+    reads for a device copy of known size), or None when no record matches the
+    current kernel sources.  Record lines: workload, source hash, bytes per
+    launch, then free text."""
     try:
         with open(TRAFFIC) as f:
-            rec = json.load(f).get(workload)
-    except (OSError, ValueError):
+            lines = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    except OSError:
         return None
-    if not rec or rec.get("source_hash") != kernel_source_hash():
-        return None
-    return int(rec["bytes_per_launch"])
+    for ln in lines:
+        if ln[0] == workload and ln[1] == kernel_source_hash(family):
+            return int(ln[2])
+    return None
 
 
 def expert_bytes(T, e: int) -> int:
@@ -151,6 +163,7 @@ def main():
 
     wl = synth.WORKLOADS[args.workload]
     prefill = wl.n_tok > 16
+    family = "prefill" if prefill else "decode"
     K = args.steps if args.steps is not None else (20 if prefill else 200)
     W = args.warmup if args.warmup is not None else (3 if prefill else 20)
     n_k = args.kernel_launches if args.kernel_launches is not None else (10 if prefill else 100)
@@ -255,44 +268,69 @@ def main():
     ms_per_step = elapsed * 1e3 / K
 
     # ---- dominant kernel: fused gate+up launch, HIP events on its stream -------------
-    hip = HipEvents()
-    pairs = [(hip.create(), hip.create()) for _ in range(n_k)]
     # A queue of 256 MiB device copies keeps the GPU busy while the launches
-    # are queued (the events then bracket back-to-back kernels); the copy is
-    # also the kernel of known size the HBM byte counters are calibrated on.
+    # are queued, so the timed launches run back to back; the copy is also the
+    # kernel of known size the HBM byte counters are calibrated on.
+    hip = HipEvents()
     src = torch.ones(1 << 26, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(48):
         dst.copy_(src)
-    for j in range(n_k):
-        vq.vq_set_kernel_events(pairs[j][0], pairs[j][1])
-        step(W + (j % K))
-    vq.vq_set_kernel_events(None, None)
-    torch.cuda.synchronize()
-    durs = np.array([hip.elapsed_ms(a, b) * 1e-3 for a, b in pairs])     # seconds
-    for a, b in pairs:
-        hip.destroy(a)
-        hip.destroy(b)
+    if prefill:
+        # ~1 ms launches: an event pair around each one (the library records
+        # them on its launch stream around the gate+up GEMM only)
+        pairs = [(hip.create(), hip.create()) for _ in range(n_k)]
+        for j in range(n_k):
+            vq.vq_set_kernel_events(pairs[j][0], pairs[j][1])
+            step(W + (j % K))
+        vq.vq_set_kernel_events(None, None)
+        torch.cuda.synchronize()
+        durs = np.array([hip.elapsed_ms(a, b) * 1e-3 for a, b in pairs])     # seconds
+        for a, b in pairs:
+            hip.destroy(a)
+            hip.destroy(b)
+        k_mean = float(durs.mean())
+        timing = f"HIP event pair around each of {n_k} launches"
+    else:
+        # ~10 us launches: per-launch event markers would add a few us each, so
+        # one event pair spans n_k back-to-back launches of the gate+up stage
+        # alone (rotating layer copies and step inputs, as in the timed steps)
+        h = torch.empty((wl.n_tok * wl.top_k, wl.inter), dtype=torch.float32, device="cuda")
+        ev0, ev1 = hip.create(), hip.create()
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        hip.record(ev0, stream)
+        for j in range(n_k):
+            i = W + (j % K)
+            G, U, _ = layers[i % L]
+            vq.vq_moe_gate_up(G, U, x_dev[i], ids_dev[i], out=h)
+        hip.record(ev1, stream)
+        torch.cuda.synchronize()
+        k_mean = hip.elapsed_ms(ev0, ev1) * 1e-3 / n_k
+        hip.destroy(ev0)
+        hip.destroy(ev1)
+        del h
+        timing = f"one HIP event pair around {n_k} back-to-back launches"
     del src, dst
-    k_mean = float(durs.mean())
     if prefill:
         kwork = np.array([gate_up_flops(W + (j % K)) for j in range(n_k)])
         achieved = float(kwork.mean() / k_mean / 1e12)
         roofline = {"bound": "mfma", "achieved": round(achieved, 1),
                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
-                    "traffic": recorded_traffic(args.workload),
+                    "traffic": recorded_traffic(args.workload, family),
                     "kernel": "vq::k_gemm (gate+up grouped GEMM, SwiGLU epilogue)",
-                    "launch_us": round(k_mean * 1e6, 2), "flops_per_launch": int(kwork.mean())}
+                    "launch_us": round(k_mean * 1e6, 2), "flops_per_launch": int(kwork.mean()),
+                    "timing": timing}
     else:
         kwork = np.array([gate_up_bytes(W + (j % K)) for j in range(n_k)])
         achieved = float(kwork.mean() / k_mean / 1e9)
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": recorded_traffic(args.workload),
+                    "traffic": recorded_traffic(args.workload, family),
                     "kernel": "vq::k_rows (gate+up+SwiGLU, fused)",
-                    "launch_us": round(k_mean * 1e6, 2), "bytes_per_launch": int(kwork.mean())}
+                    "launch_us": round(k_mean * 1e6, 2), "bytes_per_launch": int(kwork.mean()),
+                    "timing": timing}
     log(f"[bench] dominant kernel: {k_mean * 1e6:.2f} us/launch, {achieved:.1f} {roofline['unit']}")
 
     # ---- CPU oracle on a bounded sample ------------------------------------------------

@@ -22,12 +22,9 @@
 //     group's fp16 scale is applied once per group (the scale factors out of
 //     the group's sum);  the segment's partial sums meet in a butterfly.
 //
-// The same engine runs one expert (vq_expert_gemv), the routed gate+up
-// projections with the SwiGLU product fused in the epilogue, and the routed
-// down projection.  Routed launches take one grid row per (token, slot)
-// pair; a workgroup whose pair is not the first occurrence of its expert
-// exits at once, the first occurrence serves every pair routed to that
-// expert, so each expert's weights are streamed exactly once.
+// This file holds the launch logic (grid sizing, LDS layout) for the
+// persistent engine in vq_decode_impl.hpp, the slot-ordered combine and the
+// fill kernel for tensors with no stored rows.
 #include "vq_decode_impl.hpp"
 
 namespace vq {

@@ -7,15 +7,15 @@
 // of pairs inside one expert's block is not fixed (atomic slots), but no
 // output depends on it: every output row is computed on its own and the
 // final combine sums each token's slots in slot order.
+#include <algorithm>
 #include <cmath>
 
 #include "vq_prefill_impl.hpp"
 
 namespace vq {
 
-#define VQ_DECL_GEMM(N)                                                                      \
-    extern template hipError_t gemm_d<N>(int, int, int, bool, const GemmArgs &, dim3, size_t, \
-                                         hipStream_t);
+#define VQ_DECL_GEMM(N) \
+    extern template hipError_t gemm_d<N>(int, int, int, const GemmArgs &, int, hipStream_t);
 VQ_DECL_GEMM(2)
 VQ_DECL_GEMM(4)
 VQ_DECL_GEMM(8)
@@ -104,9 +104,7 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const int32_t *__restri
                                                          int32_t *__restrict__ perm,
                                                          int32_t *__restrict__ pos,
                                                          int32_t *__restrict__ tiles,
-                                                         int32_t *__restrict__ n_tiles,
-                                                         uint32_t *__restrict__ zero_buf,
-                                                         int zero_n)
+                                                         int32_t *__restrict__ n_tiles)
 {
     extern __shared__ int s[];
     int *cnt = s, *base = s + E, *fill = s + 2 * E, *toff = s + 3 * E, *scratch = s + 4 * E;
@@ -115,8 +113,6 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const int32_t *__restri
         cnt[e] = 0;
         fill[e] = 0;
     }
-    for (int i = tid; i < zero_n; i += kRouteThreads)
-        zero_buf[i] = 0u;
     __syncthreads();
     for (int q = tid; q < P; q += kRouteThreads)
         atomicAdd(&cnt[ids[q]], 1);
@@ -154,15 +150,19 @@ __global__ __launch_bounds__(kRouteThreads) void k_tiles_from_offsets(
     build_tiles(cnt, base, toff, E, mt, tiles, n_tiles, scratch);
 }
 
-// Bits of max |x| of each row (non-negative floats order like their bits).
-__global__ __launch_bounds__(256) void k_rowmax(const void *__restrict__ x, int f32, int rows,
-                                                int cols, int64_t stride,
-                                                uint32_t *__restrict__ out)
+// Each row scaled by a power of two that puts its largest magnitude in
+// [2^14, 2^15) and converted to fp16 (exact for bf16 input in fp16's normal
+// range, rounded to nearest for fp32); k[row] receives the exponent.  One
+// wave per row.
+__global__ __launch_bounds__(256) void k_rowscale(const void *__restrict__ x, int f32, int rows,
+                                                  int cols, int64_t stride, f16 *__restrict__ out,
+                                                  int32_t *__restrict__ k)
 {
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows)
         return;
+    f16 *o = out + (int64_t)row * cols;
     uint32_t mx = 0;
     if (f32) {
         const float *p = static_cast<const float *>(x) + (int64_t)row * stride;
@@ -171,24 +171,53 @@ __global__ __launch_bounds__(256) void k_rowmax(const void *__restrict__ x, int 
             mx = max(mx, max(max(q.x & 0x7fffffffu, q.y & 0x7fffffffu),
                              max(q.z & 0x7fffffffu, q.w & 0x7fffffffu)));
         }
+#pragma unroll
+        for (int o2 = 32; o2 >= 1; o2 >>= 1)
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, o2, 64));
+        const int ex = range_exponent(__uint_as_float(mx));
+        const float up = ldexpf(1.0f, ex);
+        for (int c = lane * 4; c < cols; c += 256) {
+            const float4 q = *reinterpret_cast<const float4 *>(p + c);
+            union { f16x4 v; uint2 u; } h;
+            h.v[0] = (f16)(q.x * up);
+            h.v[1] = (f16)(q.y * up);
+            h.v[2] = (f16)(q.z * up);
+            h.v[3] = (f16)(q.w * up);
+            *reinterpret_cast<uint2 *>(o + c) = h.u;
+        }
+        if (lane == 0)
+            k[row] = ex;
     } else {
         const uint16_t *p = static_cast<const uint16_t *>(x) + (int64_t)row * stride;
         for (int c = lane * 8; c < cols; c += 512) {
             const uint4 q = *reinterpret_cast<const uint4 *>(p + c);
             const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                mx = max(mx, max((w[k] & 0x7fffu) << 16, (w[k] >> 16 & 0x7fffu) << 16));
+            for (int j = 0; j < 4; ++j)
+                mx = max(mx, max((w[j] & 0x7fffu) << 16, (w[j] >> 16 & 0x7fffu) << 16));
         }
-    }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
-    if (lane == 0)
-        out[row] = mx;
+        for (int o2 = 32; o2 >= 1; o2 >>= 1)
+            mx = max(mx, (uint32_t)__shfl_xor((int)mx, o2, 64));
+        const int ex = range_exponent(__uint_as_float(mx));
+        const float up = ldexpf(1.0f, ex);
+        for (int c = lane * 8; c < cols; c += 512) {
+            const uint4 q = *reinterpret_cast<const uint4 *>(p + c);
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+            union { f16x8 v; uint4 u; } h;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                h.v[2 * j] = (f16)(__uint_as_float(w[j] << 16) * up);
+                h.v[2 * j + 1] = (f16)(__uint_as_float(w[j] & 0xffff0000u) * up);
+            }
+            *reinterpret_cast<uint4 *>(o + c) = h.u;
+        }
+        if (lane == 0)
+            k[row] = ex;
+    }
 }
 
-// y[t][c] = sum over slots s (in order) of w[t][s] * z[pos[t*k+s]][c]
+// y[t][c] = sum over slots s (in order) of w[t][s] * z[pos[t*k + s]][c].
 __global__ __launch_bounds__(256) void k_combine_perm(const float *__restrict__ z,
                                                       const int32_t *__restrict__ pos,
                                                       const float *__restrict__ w, int n_tok,
@@ -234,14 +263,26 @@ static hipError_t launch_zero(float *p, int64_t n, hipStream_t stream)
     return hipGetLastError();
 }
 
+static hipError_t launch_rowscale(const void *x, int f32, int rows, int cols, f16 *out,
+                                  int32_t *k, hipStream_t stream)
+{
+    if (rows <= 0)
+        return hipSuccess;
+    hipLaunchKernelGGL(k_rowscale, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, x, f32,
+                       rows, cols, (int64_t)cols, out, k);
+    return hipGetLastError();
+}
+
 static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-// Tile height: 192 rows when the expected largest expert block (mean + 4
-// standard deviations of a binomial count) exceeds 128, else 128.
+// Tile height (32-row blocks): the smallest compiled height that holds the
+// expected largest expert block (mean + 2 standard deviations of a binomial
+// count) in one tile.
 static int pick_mb(int64_t rows, int E)
 {
     const double mean = (double)rows / E;
-    return (mean + 4.0 * sqrt(mean) > 128.0) ? 6 : 4;
+    const double big = mean + 2.0 * sqrt(mean);
+    return big <= 64.0 ? 2 : (big <= 96.0 ? 3 : 5);
 }
 
 static int64_t max_tiles(int64_t rows, int E, int mt)
@@ -249,22 +290,39 @@ static int64_t max_tiles(int64_t rows, int E, int mt)
     return rows / mt + (rows < E ? rows : E) + 1;
 }
 
-static size_t gemm_lds_bytes(const TensorDev &t0, const TensorDev *t1, int mb, int &cb_offset1,
-                             int &a_offset)
+// LDS bytes per lane of a code window and of a launch with a three-stage
+// ring: the host mirror of BWin / GemmShape / gemm_layout.
+static int window_lds_bytes(int d, int bits)
 {
-    cb_offset1 = (t0.cb_dwords + 3) & ~3;
-    int off = t1 ? cb_offset1 + t1->cb_dwords : t0.cb_dwords;
-    off = (off + 3) & ~3;
-    a_offset = off;
-    off += 2 * 32 * mb * kAStride / 2;
-    return (size_t)off * 4;
+    const int G = 64 / d, nbits = G / 2 * bits;
+    int m = 0;
+    for (int g = 0; g < 32; ++g)
+        for (int h = 0; h < 2; ++h)
+            m = std::max(m, (g * G * bits + h * nbits) & 31);
+    const int nw = (m + nbits + 31) / 32;
+    return nw / 4 * 16 + (nw % 4 == 3 ? 16 : 4 * (nw % 4));
 }
 
-static hipError_t launch_gemm(const TensorDev &t0, const TensorDev *t1, int mb, const void *act,
-                              bool act_f32, int64_t act_stride, const int32_t *perm, int act_div,
-                              const uint32_t *amax, const int32_t *tiles, const int32_t *n_tiles,
-                              int64_t tiles_cap, float *out, int64_t out_stride,
-                              uint32_t *out_amax, hipStream_t stream)
+static size_t gemm_lds_min(const TensorDev &t, int nproj, int mb)
+{
+    const int nt = 64 * kGemmWaves, rpd = nt / 8;
+    const size_t a_bytes = (size_t)((32 * mb + rpd - 1) / rpd) * nt * 16;
+    const size_t b_bytes = (size_t)nproj * nt * (window_lds_bytes(t.d, t.bits) + 4);
+    const size_t cb = ((size_t)t.K * t.d * 2 + 15) & ~(size_t)15;
+    return nproj * cb + (size_t)32 * mb * 4 + 3 * (a_bytes + b_bytes) + 16;
+}
+
+// gate and up in one launch unless their codebooks leave no room for the ring
+static bool fused_gate_up(const TensorDev &g, int mb)
+{
+    return gemm_lds_min(g, 2, mb) <= (size_t)kLdsBudget;
+}
+
+static hipError_t launch_gemm(const TensorDev &t0, const TensorDev *t1, int mb, const f16 *act,
+                              int act_stride, const int32_t *act_k, const int32_t *perm,
+                              int act_div, const int32_t *tiles, const int32_t *n_tiles,
+                              int64_t tile_cap, float *out, int64_t out_stride,
+                              const float *gate_in, const int32_t *gate_map, hipStream_t stream)
 {
     GemmArgs a = {};
     const TensorDev *ts[2] = {&t0, t1};
@@ -274,30 +332,29 @@ static hipError_t launch_gemm(const TensorDev &t0, const TensorDev *t1, int mb, 
         a.scales[p] = ts[p]->scales;
         a.row_map[p] = ts[p]->row_map;
         a.codebook[p] = ts[p]->codebook;
-        a.cb_dwords[p] = ts[p]->cb_dwords;
+        a.cb_bytes[p] = ts[p]->K * ts[p]->d * 2;
     }
-    const size_t lds = gemm_lds_bytes(t0, t1, mb, a.cb_offset1, a.a_offset);
+    if (!t1)
+        a.row_map[1] = gate_map;
     a.rows = t0.rows;
-    a.cols = t0.cols;
     a.groups = t0.groups;
     a.wpr = t0.wpr;
     a.act = act;
     a.act_stride = act_stride;
+    a.act_k = act_k;
     a.perm = perm;
     a.act_div = act_div > 0 ? act_div : 1;
-    a.amax = amax;
     a.tiles = tiles;
     a.n_tiles = n_tiles;
+    a.gate_in = gate_in;
     a.out = out;
     a.out_stride = out_stride;
-    a.out_amax = out_amax;
-    if (tiles_cap > 65535)
+    if (tile_cap > 0x7fffffff)
         return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((t0.rows + kGemmN - 1) / kGemmN), (unsigned)tiles_cap);
     switch (t0.d) {
-    case 2: return gemm_d<2>(t0.bits, nproj, mb, act_f32, a, grid, lds, stream);
-    case 4: return gemm_d<4>(t0.bits, nproj, mb, act_f32, a, grid, lds, stream);
-    case 8: return gemm_d<8>(t0.bits, nproj, mb, act_f32, a, grid, lds, stream);
+    case 2: return gemm_d<2>(t0.bits, nproj, mb, a, (int)tile_cap, stream);
+    case 4: return gemm_d<4>(t0.bits, nproj, mb, a, (int)tile_cap, stream);
+    case 8: return gemm_d<8>(t0.bits, nproj, mb, a, (int)tile_cap, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -305,7 +362,7 @@ static hipError_t launch_gemm(const TensorDev &t0, const TensorDev *t1, int mb, 
 // ---- vq_expert_gemm ------------------------------------------------------------
 
 struct GemmWs {
-    size_t tiles, n_tiles, amax, total;
+    size_t tiles, n_tiles, xs, xk, total;
     int mb;
     int64_t cap;
 };
@@ -315,10 +372,16 @@ static GemmWs gemm_ws(const TensorDev &t, int n_x_rows)
     GemmWs w;
     w.mb = pick_mb(n_x_rows, t.n_experts);
     w.cap = max_tiles(n_x_rows, t.n_experts, 32 * w.mb);
-    w.tiles = 0;
-    w.n_tiles = align256(w.tiles + (size_t)w.cap * 3 * 4);
-    w.amax = align256(w.n_tiles + 4);
-    w.total = align256(w.amax + (size_t)n_x_rows * 4);
+    size_t o = 0;
+    w.tiles = o;
+    o = align256(o + (size_t)w.cap * 12);
+    w.n_tiles = o;
+    o = align256(o + 4);
+    w.xs = o;
+    o = align256(o + (size_t)n_x_rows * t.cols * 2);
+    w.xk = o;
+    o = align256(o + (size_t)n_x_rows * 4);
+    w.total = o;
     return w;
 }
 
@@ -334,29 +397,30 @@ hipError_t launch_expert_gemm(const TensorDev &t, int n_x_rows, const void *x, i
     if (t.n_experts > kMaxRouteExperts)
         return hipErrorNotSupported;
     const GemmWs w = gemm_ws(t, n_x_rows);
+    if (gemm_lds_min(t, 1, w.mb) > (size_t)kLdsBudget)
+        return hipErrorNotSupported;
     char *base = static_cast<char *>(ws);
     int32_t *tiles = reinterpret_cast<int32_t *>(base + w.tiles);
     int32_t *n_tiles = reinterpret_cast<int32_t *>(base + w.n_tiles);
-    uint32_t *amax = reinterpret_cast<uint32_t *>(base + w.amax);
+    f16 *xs = reinterpret_cast<f16 *>(base + w.xs);
+    int32_t *xk = reinterpret_cast<int32_t *>(base + w.xk);
     const size_t lds_t = (size_t)(3 * t.n_experts + 17) * 4;
     hipLaunchKernelGGL(k_tiles_from_offsets, dim3(1), dim3(kRouteThreads), lds_t, stream,
                        expert_offsets, t.n_experts, 32 * w.mb, tiles, n_tiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(k_rowmax, dim3((unsigned)((n_x_rows + 3) / 4)), dim3(256), 0, stream, x,
-                       x_f32, n_x_rows, t.cols, (int64_t)t.cols, amax);
-    if ((e = hipGetLastError()) != hipSuccess)
-        return e;
     if (t.n_stored == 0) {
         // every row dead: the product is exactly zero
         return launch_zero(y, (int64_t)n_x_rows * t.rows, stream);
     }
+    if ((e = launch_rowscale(x, x_f32, n_x_rows, t.cols, xs, xk, stream)) != hipSuccess)
+        return e;
     const KernelEvents &ev = kernel_events();
     if (ev.start)
         (void)hipEventRecord(ev.start, stream);
-    e = launch_gemm(t, nullptr, w.mb, x, x_f32 != 0, t.cols, nullptr, 1, amax, tiles, n_tiles,
-                    w.cap, y, t.rows, nullptr, stream);
+    e = launch_gemm(t, nullptr, w.mb, xs, t.cols, xk, nullptr, 1, tiles, n_tiles, w.cap, y, t.rows,
+                    nullptr, nullptr, stream);
     if (ev.stop)
         (void)hipEventRecord(ev.stop, stream);
     return e;
@@ -365,8 +429,9 @@ hipError_t launch_expert_gemm(const TensorDev &t, int n_x_rows, const void *x, i
 // ---- vq_moe_ffn, many tokens ---------------------------------------------------
 
 struct FfnWs {
-    size_t offs, perm, pos, tiles, n_tiles, xmax, hmax, h, z, total;
+    size_t offs, perm, pos, tiles, n_tiles, xs, xk, g, h, hs, hk, z, total;
     int mb;
+    bool fused;
     int64_t cap;
 };
 
@@ -376,25 +441,25 @@ static FfnWs ffn_ws(const TensorDev &g, const TensorDev &dn, int n_tok, int top_
     const int64_t P = (int64_t)n_tok * top_k;
     w.mb = pick_mb(P, g.n_experts);
     w.cap = max_tiles(P, g.n_experts, 32 * w.mb);
+    w.fused = fused_gate_up(g, w.mb);
     size_t o = 0;
-    w.offs = o;
-    o = align256(o + (size_t)(g.n_experts + 1) * 4);
-    w.perm = o;
-    o = align256(o + (size_t)P * 4);
-    w.pos = o;
-    o = align256(o + (size_t)P * 4);
-    w.tiles = o;
-    o = align256(o + (size_t)w.cap * 12);
-    w.n_tiles = o;
-    o = align256(o + 4);
-    w.xmax = o;
-    o = align256(o + (size_t)n_tok * 4);
-    w.hmax = o;
-    o = align256(o + (size_t)P * 4);
-    w.h = o;
-    o = align256(o + (size_t)P * g.rows * 4);
-    w.z = o;
-    o = align256(o + (size_t)P * dn.rows * 4);
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o = align256(o + bytes);
+        return at;
+    };
+    w.offs = take((size_t)(g.n_experts + 1) * 4);
+    w.perm = take((size_t)P * 4);
+    w.pos = take((size_t)P * 4);
+    w.tiles = take((size_t)w.cap * 12);
+    w.n_tiles = take(4);
+    w.xs = take((size_t)n_tok * g.cols * 2);
+    w.xk = take((size_t)n_tok * 4);
+    w.g = take(w.fused ? 0 : (size_t)P * g.rows * 4);
+    w.h = take((size_t)P * g.rows * 4);
+    w.hs = take((size_t)P * g.rows * 2);
+    w.hk = take((size_t)P * 4);
+    w.z = take((size_t)P * dn.rows * 4);
     w.total = o;
     return w;
 }
@@ -412,42 +477,57 @@ hipError_t launch_moe_prefill(const TensorDev &g, const TensorDev &u, const Tens
     if (g.n_experts > kMaxRouteExperts)
         return hipErrorNotSupported;
     const FfnWs w = ffn_ws(g, dn, n_tok, top_k);
+    if (gemm_lds_min(g, 1, w.mb) > (size_t)kLdsBudget ||
+        gemm_lds_min(dn, 1, w.mb) > (size_t)kLdsBudget)
+        return hipErrorNotSupported;
     char *base = static_cast<char *>(ws);
     int32_t *offs = reinterpret_cast<int32_t *>(base + w.offs);
     int32_t *perm = reinterpret_cast<int32_t *>(base + w.perm);
     int32_t *pos = reinterpret_cast<int32_t *>(base + w.pos);
     int32_t *tiles = reinterpret_cast<int32_t *>(base + w.tiles);
     int32_t *n_tiles = reinterpret_cast<int32_t *>(base + w.n_tiles);
-    uint32_t *xmax = reinterpret_cast<uint32_t *>(base + w.xmax);
-    uint32_t *hmax = reinterpret_cast<uint32_t *>(base + w.hmax);
+    f16 *xs = reinterpret_cast<f16 *>(base + w.xs);
+    int32_t *xk = reinterpret_cast<int32_t *>(base + w.xk);
+    float *gbuf = reinterpret_cast<float *>(base + w.g);
     float *h = reinterpret_cast<float *>(base + w.h);
+    f16 *hs = reinterpret_cast<f16 *>(base + w.hs);
+    int32_t *hk = reinterpret_cast<int32_t *>(base + w.hk);
     float *z = reinterpret_cast<float *>(base + w.z);
     const int P = n_tok * top_k;
     const int E = g.n_experts;
 
     const size_t lds_r = (size_t)(4 * E + 17) * 4;
     hipLaunchKernelGGL(k_route, dim3(1), dim3(kRouteThreads), lds_r, stream, ids, P, E,
-                       32 * w.mb, offs, perm, pos, tiles, n_tiles, hmax, P);
+                       32 * w.mb, offs, perm, pos, tiles, n_tiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(k_rowmax, dim3((unsigned)((n_tok + 3) / 4)), dim3(256), 0, stream, x,
-                       x_f32, n_tok, g.cols, (int64_t)g.cols, xmax);
-    if ((e = hipGetLastError()) != hipSuccess)
-        return e;
     if (g.n_stored == 0 || u.n_stored == 0 || dn.n_stored == 0)
         return launch_zero(y, (int64_t)n_tok * dn.rows, stream);
+    if ((e = launch_rowscale(x, x_f32, n_tok, g.cols, xs, xk, stream)) != hipSuccess)
+        return e;
     const KernelEvents &ev = kernel_events();
     if (ev.start)
         (void)hipEventRecord(ev.start, stream);
-    e = launch_gemm(g, &u, w.mb, x, x_f32 != 0, g.cols, perm, top_k, xmax, tiles, n_tiles, w.cap,
-                    h, g.rows, hmax, stream);
+    if (w.fused) {
+        e = launch_gemm(g, &u, w.mb, xs, g.cols, xk, perm, top_k, tiles, n_tiles, w.cap, h, g.rows,
+                        nullptr, nullptr, stream);
+    } else {
+        // codebooks too large for one launch: gate first, then up with SwiGLU
+        e = launch_gemm(g, nullptr, w.mb, xs, g.cols, xk, perm, top_k, tiles, n_tiles, w.cap, gbuf,
+                        g.rows, nullptr, nullptr, stream);
+        if (e == hipSuccess)
+            e = launch_gemm(u, nullptr, w.mb, xs, g.cols, xk, perm, top_k, tiles, n_tiles, w.cap,
+                            h, g.rows, gbuf, g.row_map, stream);
+    }
     if (ev.stop)
         (void)hipEventRecord(ev.stop, stream);
     if (e != hipSuccess)
         return e;
-    e = launch_gemm(dn, nullptr, w.mb, h, true, g.rows, nullptr, 1, hmax, tiles, n_tiles, w.cap, z,
-                    dn.rows, nullptr, stream);
+    if ((e = launch_rowscale(h, 1, P, g.rows, hs, hk, stream)) != hipSuccess)
+        return e;
+    e = launch_gemm(dn, nullptr, w.mb, hs, g.rows, hk, nullptr, 1, tiles, n_tiles, w.cap, z,
+                    dn.rows, nullptr, nullptr, stream);
     if (e != hipSuccess)
         return e;
     const int64_t n4 = (int64_t)n_tok * dn.rows / 4;

@@ -3,6 +3,6 @@
 
 namespace vq {
 
-template hipError_t gemm_d<4>(int, int, int, bool, const GemmArgs &, dim3, size_t, hipStream_t);
+template hipError_t gemm_d<4>(int, int, int, const GemmArgs &, int, hipStream_t);
 
 }  // namespace vq

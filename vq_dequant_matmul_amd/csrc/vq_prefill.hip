@@ -72,8 +72,9 @@ __device__ int block_exclusive_scan(int *v, int n, int *scratch)
     return total;
 }
 
-// Tiles of at most mt rows per expert, rows split evenly: tiles[t] =
-// (expert, first grouped position, rows).  cnt, offs, toff: LDS arrays of E.
+// Tiles of at most mt rows per expert: full tiles, then the remainder
+// (fewest 32-row blocks in total): tiles[t] = (expert, first grouped
+// position, rows).  cnt, offs, toff: LDS arrays of E.
 __device__ void build_tiles(const int *cnt, const int *offs, int *toff, int E, int mt,
                             int32_t *tiles, int32_t *n_tiles, int *scratch)
 {
@@ -83,15 +84,12 @@ __device__ void build_tiles(const int *cnt, const int *offs, int *toff, int E, i
     const int total = block_exclusive_scan(toff, E, scratch);
     for (int e = threadIdx.x; e < E; e += kRouteThreads) {
         const int c = cnt[e];
-        if (c == 0)
-            continue;
         const int nt = (c + mt - 1) / mt;
-        const int per = (c + nt - 1) / nt;
         for (int j = 0; j < nt; ++j) {
             const int t = toff[e] + j;
             tiles[3 * t + 0] = e;
-            tiles[3 * t + 1] = offs[e] + j * per;
-            tiles[3 * t + 2] = min(per, c - j * per);
+            tiles[3 * t + 1] = offs[e] + j * mt;
+            tiles[3 * t + 2] = min(mt, c - j * mt);
         }
     }
     if (threadIdx.x == 0)
@@ -282,7 +280,7 @@ static int pick_mb(int64_t rows, int E)
 {
     const double mean = (double)rows / E;
     const double big = mean + 2.0 * sqrt(mean);
-    return big <= 64.0 ? 2 : (big <= 96.0 ? 3 : 5);
+    return big <= 64.0 ? 2 : (big <= 128.0 ? 4 : 5);
 }
 
 static int64_t max_tiles(int64_t rows, int E, int mt)
@@ -290,32 +288,10 @@ static int64_t max_tiles(int64_t rows, int E, int mt)
     return rows / mt + (rows < E ? rows : E) + 1;
 }
 
-// LDS bytes per lane of a code window and of a launch with a three-stage
-// ring: the host mirror of BWin / GemmShape / gemm_layout.
-static int window_lds_bytes(int d, int bits)
-{
-    const int G = 64 / d, nbits = G / 2 * bits;
-    int m = 0;
-    for (int g = 0; g < 32; ++g)
-        for (int h = 0; h < 2; ++h)
-            m = std::max(m, (g * G * bits + h * nbits) & 31);
-    const int nw = (m + nbits + 31) / 32;
-    return nw / 4 * 16 + (nw % 4 == 3 ? 16 : 4 * (nw % 4));
-}
-
-static size_t gemm_lds_min(const TensorDev &t, int nproj, int mb)
-{
-    const int nt = 64 * kGemmWaves, rpd = nt / 8;
-    const size_t a_bytes = (size_t)((32 * mb + rpd - 1) / rpd) * nt * 16;
-    const size_t b_bytes = (size_t)nproj * nt * (window_lds_bytes(t.d, t.bits) + 4);
-    const size_t cb = ((size_t)t.K * t.d * 2 + 15) & ~(size_t)15;
-    return nproj * cb + (size_t)32 * mb * 4 + 3 * (a_bytes + b_bytes) + 16;
-}
-
 // gate and up in one launch unless their codebooks leave no room for the ring
 static bool fused_gate_up(const TensorDev &g, int mb)
 {
-    return gemm_lds_min(g, 2, mb) <= (size_t)kLdsBudget;
+    return gemm_fits(g.d, g.bits, 2, mb);
 }
 
 static hipError_t launch_gemm(const TensorDev &t0, const TensorDev *t1, int mb, const f16 *act,
@@ -397,7 +373,7 @@ hipError_t launch_expert_gemm(const TensorDev &t, int n_x_rows, const void *x, i
     if (t.n_experts > kMaxRouteExperts)
         return hipErrorNotSupported;
     const GemmWs w = gemm_ws(t, n_x_rows);
-    if (gemm_lds_min(t, 1, w.mb) > (size_t)kLdsBudget)
+    if (!gemm_fits(t.d, t.bits, 1, w.mb))
         return hipErrorNotSupported;
     char *base = static_cast<char *>(ws);
     int32_t *tiles = reinterpret_cast<int32_t *>(base + w.tiles);
@@ -477,8 +453,7 @@ hipError_t launch_moe_prefill(const TensorDev &g, const TensorDev &u, const Tens
     if (g.n_experts > kMaxRouteExperts)
         return hipErrorNotSupported;
     const FfnWs w = ffn_ws(g, dn, n_tok, top_k);
-    if (gemm_lds_min(g, 1, w.mb) > (size_t)kLdsBudget ||
-        gemm_lds_min(dn, 1, w.mb) > (size_t)kLdsBudget)
+    if (!gemm_fits(g.d, g.bits, 1, w.mb) || !gemm_fits(dn.d, dn.bits, 1, w.mb))
         return hipErrorNotSupported;
     char *base = static_cast<char *>(ws);
     int32_t *offs = reinterpret_cast<int32_t *>(base + w.offs);

@@ -80,6 +80,18 @@ __device__ __forceinline__ void barrier()
     asm volatile("s_barrier" : : : "memory");
 }
 
+// Calls f(integral_constant<int, i>) for i = 0 .. N-1.
+template <int... I, class F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F &&f)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
 // The packed-code window of one lane: codes CL*h + [0, CL) of a group
 // (columns 32h + [0, 32)).
 template <int D, int BITS>
@@ -132,85 +144,41 @@ struct GemmArgs {
 template <int D, int BITS, int NPROJ, int MB, int WAVES>
 struct GemmShape {
     static constexpr int NT = 64 * WAVES;
-    static constexpr int RPD = NT / 8;                          // tile rows per A load
+    // 32-row weight blocks per wave: two (each activation fragment read from
+    // LDS then feeds 2*NPROJ MFMAs) unless the accumulators would not fit
+    static constexpr int NN = (NPROJ * 2 * MB * 16 <= 256) ? 2 : 1;
+    static constexpr int NPB = NPROJ * NN;                       // (projection, block) pairs
+    static constexpr int WG_ROWS = 32 * NN * WAVES;              // weight rows per workgroup
+    static constexpr int RPD = NT / 8;                           // tile rows per A load
     static constexpr int NDMA_A = (32 * MB + RPD - 1) / RPD;
     static constexpr int A_BYTES = NDMA_A * NT * 16;
-    static constexpr int B_BYTES = NPROJ * NT * (BWin<D, BITS>::LDS_BYTES + 4);
-    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int WIN = NT * (BWin<D, BITS>::LDS_BYTES + 4);   // one (projection, block)
+    static constexpr int STAGE = A_BYTES + NPB * WIN;
     // vector-memory operations per stage and wave: scales, code windows, activations
-    static constexpr int NOPS = NDMA_A + NPROJ * (BWin<D, BITS>::NDMA + 1);
+    static constexpr int NOPS = NDMA_A + NPB * (BWin<D, BITS>::NDMA + 1);
+    // LDS: the largest codebooks (64 KiB at most each) and the tile's row
+    // factors are dynamic, the ring static; four stages when they fit
+    static constexpr int CB_MAX = ((1 << BITS) * D * 2 < 65536) ? (1 << BITS) * D * 2 : 65536;
+    static constexpr int FIXED = NPROJ * CB_MAX + 32 * MB * 4;
+    static constexpr int S = (FIXED + 4 * STAGE <= kLdsBudget) ? 4 : 3;
+    static constexpr bool FITS = FIXED + S * STAGE <= kLdsBudget;
 };
 
-// One lane's B operand of one projection for one group: 4 slices x 8 halves,
-// w = fp16(scale * entry).
-template <int D, int BITS>
-__device__ __forceinline__ void decode_b(const uint32_t (&nw)[BWin<D, BITS>::NW], uint32_t sc,
-                                         const uint32_t *__restrict__ cb, f16x8 (&bf)[4])
-{
-    using BW = BWin<D, BITS>;
-    union { uint32_t u; f16x2 h; } s2;
-    s2.u = sc * 0x10001u;
-    constexpr uint32_t mask = (1u << BITS) - 1u;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        union { f16x8 v; f16x2 p[4]; uint32_t u[4]; } o;
-#pragma unroll
-        for (int c = 0; c < BW::PER; ++c) {
-            const int t = j * BW::PER + c;            // compile-time code position
-            const int pb = t * BITS;
-            const int wi = pb >> 5, bsh = pb & 31;
-            const uint32_t code = (bsh + BITS <= 32)
-                                      ? __builtin_amdgcn_ubfe(nw[wi], bsh, BITS)
-                                      : (__builtin_amdgcn_alignbit(nw[wi + 1], nw[wi], bsh) & mask);
-            if constexpr (D == 2) {
-                o.u[c] = cb[code];
-            } else if constexpr (D == 4) {
-                const uint2 q = *reinterpret_cast<const uint2 *>(cb + 2 * code);
-                o.u[2 * c] = q.x;
-                o.u[2 * c + 1] = q.y;
-            } else {
-                const uint4 q = *reinterpret_cast<const uint4 *>(cb + 4 * code);
-                o.u[0] = q.x;
-                o.u[1] = q.y;
-                o.u[2] = q.z;
-                o.u[3] = q.w;
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            o.p[k] = o.p[k] * s2.h;                   // v_pk_mul_f16: fp16(s * c)
-        bf[j] = o.v;
-    }
-}
-
-template <int D, int BITS, int NPROJ, int MB, int WAVES, int S>
+template <int D, int BITS, int NPROJ, int MB, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
 {
     using BW = BWin<D, BITS>;
     using SH = GemmShape<D, BITS, NPROJ, MB, WAVES>;
     constexpr int NT = SH::NT;
     constexpr int NW = BW::NW;
-    static_assert(S >= 3, "the ring needs three stages");
-    // codebooks and row factors: dynamic LDS; the ring: one static array per
-    // stage, so the compiler can tell a stage being filled from the stages
-    // being read and waits only for the loads a read depends on
+    constexpr int S = SH::S;
+    constexpr int NN = SH::NN;
+    constexpr int NPB = SH::NPB;
+    if constexpr (SH::FITS) {
+    // codebooks and row factors: dynamic LDS; the ring of S stages: static
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
     char *const lb = reinterpret_cast<char *>(lds);
-    __shared__ __attribute__((aligned(16))) char ring0[SH::STAGE];
-    __shared__ __attribute__((aligned(16))) char ring1[SH::STAGE];
-    __shared__ __attribute__((aligned(16))) char ring2[SH::STAGE];
-    __shared__ __attribute__((aligned(16))) char ring3[S > 3 ? SH::STAGE : 16];
-    auto ring = [&](auto K) -> char * {
-        constexpr int k = decltype(K)::value;
-        if constexpr (k == 0)
-            return ring0;
-        else if constexpr (k == 1)
-            return ring1;
-        else if constexpr (k == 2)
-            return ring2;
-        else
-            return ring3;
-    };
+    __shared__ __attribute__((aligned(16))) char ring[S * SH::STAGE];
 
     // Workgroup L runs on XCD L % 8 (round-robin dispatch); all weight-row
     // tiles of M tile t run on XCD t % 8 one after another, so the tile's
@@ -230,7 +198,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
     const int m0 = a.tiles[3 * tile + 1];
     const int mlen = a.tiles[3 * tile + 2];
     const int nblk = (mlen + 31) >> 5;
-    const int n = ntile * (32 * WAVES) + 32 * wave + (lane & 31);   // this lane's weight row
+    // weight row of block nb of this lane: nrow0 + 32 * nb
+    const int nrow0 = ntile * SH::WG_ROWS + wave * 32 * NN + (lane & 31);
     const int G = a.groups;
 
     // ---- prologue: codebooks, row factors, per-lane sources ------------------------
@@ -262,126 +231,167 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
         const int chunk = (tid & 7) ^ ((tid >> 3) & 7);
         aoff[q] = (uint32_t)row * (uint32_t)a.act_stride * 2u + (uint32_t)chunk * 16u;
     }
-    // weight rows
-    const int64_t lin = (int64_t)e * a.rows + min(n, a.rows - 1);
-    const uint32_t *brow[NPROJ];
-    const uint16_t *srow[NPROJ];
+    // weight rows, per (projection p, block nb): index pb = p * NN + nb
+    const uint32_t *brow[NPB];
+    const uint16_t *srow[NPB];
     int live = 0;
 #pragma unroll
     for (int p = 0; p < NPROJ; ++p) {
-        const int s = a.row_map[p] ? a.row_map[p][lin] : (int)lin;
-        const bool lv = (n < a.rows) && (s >= 0);
-        live |= lv ? (1 << p) : 0;
-        const int64_t sr = lv ? s : 0;
-        brow[p] = a.codes[p] + sr * a.wpr;
-        srow[p] = a.scales[p] + sr * a.groups;
-    }
-    if constexpr (NPROJ == 1) {
-        if (a.gate_in && a.row_map[1] && a.row_map[1][lin] < 0)
-            live = 0;   // split SwiGLU: a dead gate row gives h = +0.0
+#pragma unroll
+        for (int nb = 0; nb < NN; ++nb) {
+            const int n = nrow0 + 32 * nb;
+            const int64_t lin = (int64_t)e * a.rows + min(n, a.rows - 1);
+            const int s = a.row_map[p] ? a.row_map[p][lin] : (int)lin;
+            bool lv = (n < a.rows) && (s >= 0);
+            if (NPROJ == 1 && a.gate_in && a.row_map[1] && a.row_map[1][lin] < 0)
+                lv = false;   // split SwiGLU: a dead gate row gives h = +0.0
+            const int pb = p * NN + nb;
+            live |= lv ? (1 << pb) : 0;
+            const int64_t sr = lv ? s : 0;
+            brow[pb] = a.codes[p] + sr * a.wpr;
+            srow[pb] = a.scales[p] + sr * a.groups;
+        }
     }
 
-    // ---- one stage of loads: scales and code windows, then activations -------------
-    auto issue = [&](int gg, char *sb) {
-        char *bb = sb + SH::A_BYTES;
-        const int sbit = gg * BW::G * BITS + h * BW::NBITS;
-        const int ws = min(sbit >> 5, a.wpr - NW);   // window start, kept inside the row
-#pragma unroll
-        for (int p = 0; p < NPROJ; ++p) {
-            // the aligned dword holding the scale (it never crosses a page)
-            const uintptr_t sp = reinterpret_cast<uintptr_t>(srow[p] + gg);
-            dma<4>(reinterpret_cast<const void *>(sp & ~(uintptr_t)3), bb + wave * 64 * 4);
-            bb += NT * 4;
-            const uint32_t *wp = brow[p] + ws;
-#pragma unroll
-            for (int k = 0; k < BW::N16; ++k) {
-                dma<16>(wp + 4 * k, bb + wave * 64 * 16);
-                bb += NT * 16;
-            }
-            if constexpr (BW::TAIL == 3) {
-                dma<12>(wp + 4 * BW::N16, bb + wave * 64 * 16);
-                bb += NT * 16;
+    // ---- loads of one stage, one instruction per unit: per (projection, block)
+    // the scale and the code window, then the activation rows ---------------------------
+    constexpr int PB = BW::NDMA + 1;                     // loads per (projection, block)
+    auto dma_unit = [&](auto Q, int gg, char *sb) {
+        constexpr int q = decltype(Q)::value;
+        if constexpr (q < NPB * PB) {
+            constexpr int pb = q / PB, r = q % PB;
+            char *bb = sb + SH::A_BYTES + pb * SH::WIN;
+            if constexpr (r == 0) {
+                // the aligned dword holding the scale (it never crosses a page)
+                const uintptr_t sp = reinterpret_cast<uintptr_t>(srow[pb] + gg);
+                dma<4>(reinterpret_cast<const void *>(sp & ~(uintptr_t)3), bb + wave * 64 * 4);
             } else {
-#pragma unroll
-                for (int k = 0; k < BW::TAIL; ++k) {
-                    dma<4>(wp + 4 * BW::N16 + k, bb + wave * 64 * 4);
-                    bb += NT * 4;
-                }
+                const int sbit = gg * BW::G * BITS + h * BW::NBITS;
+                const int ws = min(sbit >> 5, a.wpr - NW);   // window kept inside the row
+                const uint32_t *wp = brow[pb] + ws;
+                constexpr int c = r - 1;
+                if constexpr (c < BW::N16)
+                    dma<16>(wp + 4 * c, bb + NT * 4 + c * NT * 16 + wave * 64 * 16);
+                else if constexpr (BW::TAIL == 3)
+                    dma<12>(wp + 4 * c, bb + NT * 4 + c * NT * 16 + wave * 64 * 16);
+                else
+                    dma<4>(wp + 4 * BW::N16 + (c - BW::N16),
+                           bb + NT * 4 + BW::N16 * NT * 16 + (c - BW::N16) * NT * 4 + wave * 64 * 4);
             }
+        } else {
+            constexpr int qa = q - NPB * PB;
+            dma<16>(reinterpret_cast<const char *>(a.act) + (size_t)gg * 128 + aoff[qa],
+                    sb + qa * NT * 16 + wave * 1024);
         }
-        const char *ab = reinterpret_cast<const char *>(a.act) + (size_t)gg * 128;
-#pragma unroll
-        for (int q = 0; q < SH::NDMA_A; ++q)
-            dma<16>(ab + aoff[q], sb + q * NT * 16 + wave * 1024);
+    };
+    auto issue_all = [&](int gg, char *sb) {
+        static_for<SH::NOPS>([&](auto Q) { dma_unit(Q, gg, sb); });
     };
 
-    // ---- this lane's B operands of group gg, from stage st --------------------------
-    auto decode = [&](int gg, const char *sb, f16x8 (&bf)[NPROJ][4]) {
-        const char *bb = sb + SH::A_BYTES;
+    // ---- decoding this lane's B operands, in pieces -----------------------------------
+    struct Raw {
+        uint32_t w[NW];
+        uint32_t sw;
+    };
+    // raw: the scale dword and code words of (projection, block) pb
+    auto read_raw = [&](int pb, const char *sb, Raw &rw) {
+        const char *bb = sb + SH::A_BYTES + pb * SH::WIN;
+        rw.sw = *reinterpret_cast<const uint32_t *>(bb + tid * 4);
+        bb += NT * 4;
+#pragma unroll
+        for (int k = 0; k < BW::N16; ++k) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(bb + tid * 16);
+            rw.w[4 * k] = v.x;
+            rw.w[4 * k + 1] = v.y;
+            rw.w[4 * k + 2] = v.z;
+            rw.w[4 * k + 3] = v.w;
+            bb += NT * 16;
+        }
+        if constexpr (BW::TAIL == 3) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(bb + tid * 16);
+            rw.w[4 * BW::N16] = v.x;
+            rw.w[4 * BW::N16 + 1] = v.y;
+            rw.w[4 * BW::N16 + 2] = v.z;
+        } else {
+#pragma unroll
+            for (int k = 0; k < BW::TAIL; ++k)
+                rw.w[4 * BW::N16 + k] = *reinterpret_cast<const uint32_t *>(bb + tid * 4 + k * NT * 4);
+        }
+    };
+    // shift: the words realigned so the lane's first code is at bit 0, and
+    // the (s, s) multiplier (0 for a dead row)
+    auto shift_raw = [&](int pb, int gg, const Raw &rw, uint32_t (&nw)[NW], f16x2 &s2) {
         const int sbit = gg * BW::G * BITS + h * BW::NBITS;
         const int w0 = sbit >> 5;
         const int delta = w0 - min(w0, a.wpr - NW);   // > 0 only near a row's end
         const int o = sbit & 31;
+        uint32_t w[NW];
 #pragma unroll
-        for (int p = 0; p < NPROJ; ++p) {
-            const uint32_t sw = *reinterpret_cast<const uint32_t *>(bb + tid * 4);
-            bb += NT * 4;
-            const bool hi = (reinterpret_cast<uintptr_t>(srow[p] + gg) & 2) != 0;
-            const uint32_t sc = (live >> p & 1) ? (hi ? sw >> 16 : sw & 0xffffu) : 0u;
-            uint32_t w[NW];
+        for (int i = 0; i < NW; ++i)
+            w[i] = rw.w[i];
+        if (__builtin_expect(delta != 0, 0)) {
+            // the window was pulled back to stay inside the row
+            uint32_t t[NW];
 #pragma unroll
-            for (int k = 0; k < BW::N16; ++k) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(bb + tid * 16);
-                w[4 * k] = v.x;
-                w[4 * k + 1] = v.y;
-                w[4 * k + 2] = v.z;
-                w[4 * k + 3] = v.w;
-                bb += NT * 16;
+            for (int i = 0; i < NW; ++i) {
+                uint32_t v = w[NW - 1];
+#pragma unroll
+                for (int d = NW - 1; d >= 1; --d)
+                    if (i + d < NW)
+                        v = (delta == d) ? w[i + d] : v;
+                t[i] = v;
             }
-            if constexpr (BW::TAIL == 3) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(bb + tid * 16);
-                w[4 * BW::N16] = v.x;
-                w[4 * BW::N16 + 1] = v.y;
-                w[4 * BW::N16 + 2] = v.z;
-                bb += NT * 16;
-            } else {
-#pragma unroll
-                for (int k = 0; k < BW::TAIL; ++k) {
-                    w[4 * BW::N16 + k] = *reinterpret_cast<const uint32_t *>(bb + tid * 4);
-                    bb += NT * 4;
-                }
-            }
-            if (__builtin_expect(delta != 0, 0)) {
-                // the window was pulled back to stay inside the row: realign
-                uint32_t t[NW];
-#pragma unroll
-                for (int i = 0; i < NW; ++i) {
-                    uint32_t v = w[NW - 1];
-#pragma unroll
-                    for (int d = NW - 1; d >= 1; --d)
-                        if (i + d < NW)
-                            v = (delta == d) ? w[i + d] : v;
-                    t[i] = v;
-                }
-#pragma unroll
-                for (int i = 0; i < NW; ++i)
-                    w[i] = t[i];
-            }
-            uint32_t nw[NW];
 #pragma unroll
             for (int i = 0; i < NW; ++i)
-                nw[i] = __builtin_amdgcn_alignbit(i + 1 < NW ? w[i + 1] : 0u, w[i], o);
-            decode_b<D, BITS>(nw, sc, reinterpret_cast<const uint32_t *>(lb + a.cb_off[p]),
-                              bf[p]);
+                w[i] = t[i];
         }
+#pragma unroll
+        for (int i = 0; i < NW; ++i)
+            nw[i] = __builtin_amdgcn_alignbit(i + 1 < NW ? w[i + 1] : 0u, w[i], o);
+        const bool hi = (reinterpret_cast<uintptr_t>(srow[pb] + gg) & 2) != 0;
+        const uint32_t sc = (live >> pb & 1) ? (hi ? rw.sw >> 16 : rw.sw & 0xffffu) : 0u;
+        union { uint32_t u; f16x2 h; } c2;
+        c2.u = sc * 0x10001u;
+        s2 = c2.h;
     };
-
-    f32x16 acc[NPROJ][MB];
+    // lookup: the codebook entries of slice j (unscaled)
+    auto lookup = [&](int p, int j, const uint32_t (&nw)[NW], f16x8 &o) {
+        const uint32_t *cb = reinterpret_cast<const uint32_t *>(lb + a.cb_off[p]);
+        constexpr uint32_t mask = (1u << BITS) - 1u;
+        union { f16x8 v; uint32_t u[4]; } r;
 #pragma unroll
-    for (int p = 0; p < NPROJ; ++p)
+        for (int c = 0; c < BW::PER; ++c) {
+            const int t = j * BW::PER + c;
+            const int pbit = t * BITS;
+            const int wi = pbit >> 5, bsh = pbit & 31;
+            const uint32_t code = (bsh + BITS <= 32)
+                                      ? __builtin_amdgcn_ubfe(nw[wi], bsh, BITS)
+                                      : (__builtin_amdgcn_alignbit(nw[wi + 1], nw[wi], bsh) & mask);
+            if constexpr (D == 2) {
+                r.u[c] = cb[code];
+            } else if constexpr (D == 4) {
+                const uint2 q = *reinterpret_cast<const uint2 *>(cb + 2 * code);
+                r.u[2 * c] = q.x;
+                r.u[2 * c + 1] = q.y;
+            } else {
+                const uint4 q = *reinterpret_cast<const uint4 *>(cb + 4 * code);
+                r.u[0] = q.x;
+                r.u[1] = q.y;
+                r.u[2] = q.z;
+                r.u[3] = q.w;
+            }
+        }
+        o = r.v;
+    };
+    // scale: w = fp16(s * entry), v_pk_mul_f16
+    auto scale = [&](f16x8 &o, f16x2 s2) {
+        union { f16x8 v; f16x2 q[4]; } r;
+        r.v = o;
 #pragma unroll
-        for (int b = 0; b < MB; ++b)
-            acc[p][b] = f32x16{};
+        for (int k = 0; k < 4; ++k)
+            r.q[k] = r.q[k] * s2;
+        o = r.v;
+    };
 
     // A fragment of block b, slice j: tile row 32b + lane%32, columns
     // 32h + 8j + [0, 8) = chunk 4h + j, stored at chunk ^ (row % 8)
@@ -390,95 +400,155 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
     for (int j = 0; j < 4; ++j)
         swz[j] = (lane & 31) * 128 + (((4 * h + j) ^ (lane & 7)) << 4);
 
-    auto mfmas = [&](const char *ab, const f16x8 (&bf)[NPROJ][4]) {
+    // ---- the K loop for a tile of NB blocks ---------------------------------------------
+    // Step g: wait until group g's activations and group g+1's codes have
+    // landed (the later S-3 stages and group g+1's activations may still be
+    // in flight), barrier (no wave still reads stage g-1), then slice by
+    // slice: the MFMAs of group g's slice j, the codebook lookups of group
+    // g+1's slice j into the registers those MFMAs just read, the scaling
+    // of group g+1's slice j-1, and a quarter of the loads of group g+S-1
+    // into stage g-1 (past the end: the last group again, never read).
+    auto body = [&](auto NBc) {
+        constexpr int NB = decltype(NBc)::value;
+        f32x16 acc[NPB][NB];
 #pragma unroll
-        for (int b = 0; b < MB; ++b) {
-            if (b < nblk) {
+        for (int pb = 0; pb < NPB; ++pb)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const f16x8 av = *reinterpret_cast<const f16x8 *>(ab + b * 4096 + swz[j]);
+            for (int b = 0; b < NB; ++b)
+                acc[pb][b] = f32x16{};
+
+        issue_all(0, ring);
+        issue_all(min(1, G - 1), ring + SH::STAGE);
+        if constexpr (S > 3)
+            issue_all(min(2, G - 1), ring + 2 * SH::STAGE);
+        // group 0's codes and scales (its activations and the later stages
+        // may still be in flight); the barrier also publishes the codebooks
+        // and the row factors
+        wait_vm<SH::NDMA_A + (S - 2) * SH::NOPS>();
+        wait_lds();
+        barrier();
+        f16x8 bf[NPB][4];
 #pragma unroll
-                    for (int p = 0; p < NPROJ; ++p)
-                        acc[p][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, bf[p][j], acc[p][b],
-                                                                           0, 0, 0);
+        for (int pb = 0; pb < NPB; ++pb) {
+            Raw rw;
+            uint32_t nw[NW];
+            f16x2 s2;
+            read_raw(pb, ring, rw);
+            shift_raw(pb, 0, rw, nw, s2);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                lookup(pb / NN, j, nw, bf[pb][j]);
+                scale(bf[pb][j], s2);
+            }
+        }
+
+        int st = 0;   // stage of group g
+        for (int g = 0; g < G; ++g) {
+            const int st_next = (st + 1 == S) ? 0 : st + 1;
+            const int st_fill = (st == 0) ? S - 1 : st - 1;
+            const char *sa = ring + st * SH::STAGE;
+            const char *sn = ring + st_next * SH::STAGE;
+            char *sf = ring + st_fill * SH::STAGE;
+            const int gf = min(g + S - 1, G - 1);
+            const int gn = min(g + 1, G - 1);
+            wait_vm<SH::NDMA_A + (S - 3) * SH::NOPS>();
+            barrier();
+
+            Raw rw[NPB];
+            uint32_t nw[NPB][NW];
+            f16x2 s2[NPB];
+            f16x8 af[2][NB];
+#pragma unroll
+            for (int pb = 0; pb < NPB; ++pb)
+                read_raw(pb, sn, rw[pb]);
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+                af[0][b] = *reinterpret_cast<const f16x8 *>(sa + b * 4096 + swz[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            static_for<4>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                if constexpr (j < 3) {
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+                        af[(j + 1) & 1][b] =
+                            *reinterpret_cast<const f16x8 *>(sa + b * 4096 + swz[j + 1]);
+                }
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int pb = 0; pb < NPB; ++pb)
+                        acc[pb][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][b], bf[pb][j],
+                                                                            acc[pb][b], 0, 0, 0);
+                // a quarter of the next stage's loads
+                constexpr int q0 = (j * SH::NOPS) / 4, q1 = ((j + 1) * SH::NOPS) / 4;
+                static_for<q1 - q0>([&](auto Q) {
+                    dma_unit(std::integral_constant<int, q0 + decltype(Q)::value>{}, gf, sf);
+                });
+                if constexpr (j == 0) {
+#pragma unroll
+                    for (int pb = 0; pb < NPB; ++pb)
+                        shift_raw(pb, gn, rw[pb], nw[pb], s2[pb]);
+                }
+#pragma unroll
+                for (int pb = 0; pb < NPB; ++pb)
+                    lookup(pb / NN, j, nw[pb], bf[pb][j]);
+                if constexpr (j > 0) {
+#pragma unroll
+                    for (int pb = 0; pb < NPB; ++pb)
+                        scale(bf[pb][j - 1], s2[pb]);
+                }
+                // interleave the side work with the MFMAs of this slice
+                static_for<NB * NPB>([&](auto) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+#pragma unroll
+            for (int pb = 0; pb < NPB; ++pb)
+                scale(bf[pb][3], s2[pb]);
+            st = st_next;
+        }
+        // nothing may land in LDS after the workgroup ends
+        wait_vm<0>();
+
+        // ---- epilogue: lane holds D[8*(r/4) + 4*h + r%4][lane%32] of each block -----
+#pragma unroll
+        for (int nb = 0; nb < NN; ++nb) {
+            const int n = nrow0 + 32 * nb;
+            const bool colok = n < a.rows;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int i = 32 * b + 8 * (r / 4) + 4 * h + (r % 4);
+                    if (!(colok && i < mlen))
+                        continue;
+                    const float f = kf[i];
+                    const int64_t o = (int64_t)(m0 + i) * a.out_stride + n;
+                    float v;
+                    if constexpr (NPROJ == 2) {
+                        v = ((live >> nb & 1) && (live >> (NN + nb) & 1))
+                                ? silu_mul(acc[nb][b][r] * f, acc[NN + nb][b][r] * f)
+                                : 0.0f;
+                    } else {
+                        if (a.gate_in)
+                            v = (live >> nb & 1) ? silu_mul(a.gate_in[o], acc[nb][b][r] * f) : 0.0f;
+                        else
+                            v = (live >> nb & 1) ? acc[nb][b][r] * f : 0.0f;
+                    }
+                    a.out[o] = v;
                 }
             }
         }
     };
-
-    // ---- the ring ---------------------------------------------------------------------
-    issue(0, ring0);
-    issue(min(1, G - 1), ring1);
-    if constexpr (S > 3)
-        issue(min(2, G - 1), ring2);
-    // group 0's codes and scales (its activations and the later stages may
-    // still be in flight); the barrier also publishes the codebooks and the
-    // row factors
-    wait_vm<SH::NDMA_A + (S - 2) * SH::NOPS>();
-    wait_lds();
-    barrier();
-
-    f16x8 bfa[NPROJ][4], bfb[NPROJ][4];
-    decode(0, ring0, bfa);
-    // Group g: its activations and group g+1's codes must have landed (the
-    // later S-3 stages and group g+1's activations may still be in flight).
-    // After the barrier no wave still reads stage g-1, which is refilled with
-    // group g+S-1 (past the end: the last group again, never read).  The loop
-    // is unrolled so that stage and buffer indices are compile-time.
-    constexpr int U = (S % 2 == 0) ? S : 2 * S;
-    auto step = [&](auto K, int g) {
-        constexpr int k = decltype(K)::value;
-        constexpr int st = k % S, st_next = (k + 1) % S, st_fill = (k + S - 1) % S;
-        wait_vm<SH::NDMA_A + (S - 3) * SH::NOPS>();
-        barrier();
-        issue(min(g + S - 1, G - 1), ring(std::integral_constant<int, st_fill>{}));
-        if constexpr (k % 2 == 0) {
-            if (g + 1 < G)
-                decode(g + 1, ring(std::integral_constant<int, st_next>{}), bfb);
-            mfmas(ring(std::integral_constant<int, st>{}), bfa);
-        } else {
-            if (g + 1 < G)
-                decode(g + 1, ring(std::integral_constant<int, st_next>{}), bfa);
-            mfmas(ring(std::integral_constant<int, st>{}), bfb);
-        }
-    };
-    auto unrolled = [&](int g0, auto... K) { ((g0 + decltype(K)::value < G ? step(K, g0 + decltype(K)::value) : void()), ...); };
-    for (int g0 = 0; g0 < G; g0 += U) {
-        if constexpr (U == 4)
-            unrolled(g0, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{},
-                     std::integral_constant<int, 2>{}, std::integral_constant<int, 3>{});
-        else
-            unrolled(g0, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{},
-                     std::integral_constant<int, 2>{}, std::integral_constant<int, 3>{},
-                     std::integral_constant<int, 4>{}, std::integral_constant<int, 5>{});
-    }
-    // nothing may land in LDS after the workgroup ends
-    wait_vm<0>();
-
-    // ---- epilogue: lane holds D[8*(r/4) + 4*h + r%4][lane%32] of each block ---------
-    const bool colok = n < a.rows;
-#pragma unroll
-    for (int b = 0; b < MB; ++b) {
-        if (b >= nblk)
-            continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = 32 * b + 8 * (r / 4) + 4 * h + (r % 4);
-            if (!(colok && i < mlen))
-                continue;
-            const float f = kf[i];
-            const int64_t o = (int64_t)(m0 + i) * a.out_stride + n;
-            float v;
-            if constexpr (NPROJ == 2) {
-                v = (live == 3) ? silu_mul(acc[0][b][r] * f, acc[1][b][r] * f) : 0.0f;
-            } else {
-                if (a.gate_in)
-                    v = (live & 1) ? silu_mul(a.gate_in[o], acc[0][b][r] * f) : 0.0f;
-                else
-                    v = (live & 1) ? acc[0][b][r] * f : 0.0f;
-            }
-            a.out[o] = v;
-        }
+    // one specialisation per block count keeps the step free of branches
+    static_for<MB>([&](auto I) {
+        constexpr int nb = decltype(I)::value + 1;
+        if (nblk == nb)
+            body(std::integral_constant<int, nb>{});
+    });
     }
 }
 
@@ -486,12 +556,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
 
 constexpr int kGemmWaves = 4;
 
-// Dynamic LDS of one launch (codebooks, row factors); the ring of S stages is
-// static.
-template <int D, int BITS, int NPROJ, int MB, int S>
+// Dynamic LDS of one launch: codebooks, row factors (the ring is static).
+template <int NPROJ, int MB>
 inline size_t gemm_layout(GemmArgs &a)
 {
-    using SH = GemmShape<D, BITS, NPROJ, MB, kGemmWaves>;
     size_t off = 0;
     for (int p = 0; p < NPROJ; ++p) {
         a.cb_off[p] = (int)off;
@@ -502,37 +570,34 @@ inline size_t gemm_layout(GemmArgs &a)
     return off;
 }
 
-// Returns hipErrorOutOfMemory when even a three-stage ring does not fit next
-// to the codebooks (the caller then splits the projections).
+// hipErrorOutOfMemory: this geometry's codebooks leave no room for the ring
+// (the caller then splits gate and up into two launches).
 template <int D, int BITS, int NPROJ, int MB>
 static hipError_t gemm_launch(GemmArgs a, int tile_cap, hipStream_t stream)
 {
     constexpr int WAVES = kGemmWaves;
     using SH = GemmShape<D, BITS, NPROJ, MB, WAVES>;
-    const size_t lds = gemm_layout<D, BITS, NPROJ, MB, 4>(a);
-    int S = 4;
-    const void *kern = reinterpret_cast<const void *>(k_gemm<D, BITS, NPROJ, MB, WAVES, 4>);
-    if (lds + 4 * (size_t)SH::STAGE > (size_t)kLdsBudget) {
-        S = 3;
-        kern = reinterpret_cast<const void *>(k_gemm<D, BITS, NPROJ, MB, WAVES, 3>);
-    }
-    if (lds + S * (size_t)SH::STAGE + 16 > (size_t)kLdsBudget)
+    if constexpr (!SH::FITS) {
         return hipErrorOutOfMemory;
-    if (lds > 65536) {
-        hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)lds);
-        if (err != hipSuccess)
-            return err;
+    } else {
+        const size_t lds = gemm_layout<NPROJ, MB>(a);
+        const void *kern = reinterpret_cast<const void *>(k_gemm<D, BITS, NPROJ, MB, WAVES>);
+        if (lds > 65536) {
+            hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+            if (err != hipSuccess)
+                return err;
+        }
+        a.n_ntiles = (a.rows + SH::WG_ROWS - 1) / SH::WG_ROWS;
+        const int64_t wgs = (int64_t)((tile_cap + 7) / 8) * 8 * a.n_ntiles;
+        if (wgs > 0x7fffffff)
+            return hipErrorInvalidValue;
+        void *args[] = {&a};
+        return hipLaunchKernel(kern, dim3((unsigned)wgs), dim3(64 * WAVES), args, lds, stream);
     }
-    a.n_ntiles = (a.rows + 32 * WAVES - 1) / (32 * WAVES);
-    const int64_t wgs = (int64_t)((tile_cap + 7) / 8) * 8 * a.n_ntiles;
-    if (wgs > 0x7fffffff)
-        return hipErrorInvalidValue;
-    void *args[] = {&a};
-    return hipLaunchKernel(kern, dim3((unsigned)wgs), dim3(64 * WAVES), args, lds, stream);
 }
 
-// Tile heights compiled: 32 * {2, 3, 5} rows.
+// Tile heights compiled: 32 * {2, 4, 5} rows.
 template <int D, int BITS>
 struct GemmD {
     static hipError_t run(int nproj, int mb, const GemmArgs &a, int cap, hipStream_t s)
@@ -540,17 +605,49 @@ struct GemmD {
         if (nproj == 2) {
             switch (mb) {
             case 2: return gemm_launch<D, BITS, 2, 2>(a, cap, s);
-            case 3: return gemm_launch<D, BITS, 2, 3>(a, cap, s);
+            case 4: return gemm_launch<D, BITS, 2, 4>(a, cap, s);
             default: return gemm_launch<D, BITS, 2, 5>(a, cap, s);
             }
         }
         switch (mb) {
         case 2: return gemm_launch<D, BITS, 1, 2>(a, cap, s);
-        case 3: return gemm_launch<D, BITS, 1, 3>(a, cap, s);
+        case 4: return gemm_launch<D, BITS, 1, 4>(a, cap, s);
         default: return gemm_launch<D, BITS, 1, 5>(a, cap, s);
         }
     }
 };
+
+// Whether a launch of this geometry fits in LDS (host side of GemmShape::FITS).
+template <int D, int BITS>
+inline bool gemm_fits_db(int nproj, int mb)
+{
+    constexpr int W = kGemmWaves;
+    if (nproj == 2)
+        return mb == 2 ? GemmShape<D, BITS, 2, 2, W>::FITS
+                       : (mb == 4 ? GemmShape<D, BITS, 2, 4, W>::FITS : GemmShape<D, BITS, 2, 5, W>::FITS);
+    return mb == 2 ? GemmShape<D, BITS, 1, 2, W>::FITS
+                   : (mb == 4 ? GemmShape<D, BITS, 1, 4, W>::FITS : GemmShape<D, BITS, 1, 5, W>::FITS);
+}
+
+template <int D>
+inline bool gemm_fits_d(int bits, int nproj, int mb)
+{
+    switch (bits) {
+    case 8: return gemm_fits_db<D, 8>(nproj, mb);
+    case 9: return gemm_fits_db<D, 9>(nproj, mb);
+    case 10: return gemm_fits_db<D, 10>(nproj, mb);
+    case 11: return gemm_fits_db<D, 11>(nproj, mb);
+    case 12: return gemm_fits_db<D, 12>(nproj, mb);
+    case 13: return gemm_fits_db<D, 13>(nproj, mb);
+    default: return false;
+    }
+}
+
+inline bool gemm_fits(int d, int bits, int nproj, int mb)
+{
+    return d == 2 ? gemm_fits_d<2>(bits, nproj, mb)
+                  : (d == 4 ? gemm_fits_d<4>(bits, nproj, mb) : gemm_fits_d<8>(bits, nproj, mb));
+}
 
 template <int D>
 hipError_t gemm_d(int bits, int nproj, int mb, const GemmArgs &a, int cap, hipStream_t s)

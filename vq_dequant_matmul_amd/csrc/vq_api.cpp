@@ -440,6 +440,11 @@ VQ_EXPORT vq_status vq_moe_ffn(const vq_tensor *gate, const vq_tensor *up, const
     hipError_t e = launch_gate_up(g, u, n_tokens, top_k, x, x_dtype == VQ_F32, topk_ids, h, s);
     if (e != hipSuccess)
         return hip_fail(e, "vq_moe_ffn (gate/up)");
+    if (vq::mix_supported(dn, n_tokens, top_k)) {
+        // down projection and combine in one pass over the output rows
+        e = vq::launch_mix(dn, n_tokens, top_k, h, topk_ids, topk_weights, y, s);
+        return e == hipSuccess ? ok() : hip_fail(e, "vq_moe_ffn (down+combine)");
+    }
     e = launch_down(dn, n_tokens, top_k, h, topk_ids, z, s);
     if (e != hipSuccess)
         return hip_fail(e, "vq_moe_ffn (down)");

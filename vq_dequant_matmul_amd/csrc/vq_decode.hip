@@ -34,7 +34,8 @@ namespace vq {
 #define VQ_DECL_D(N)                                                                         \
     extern template hipError_t rows_d<N>(int, const RowsArgs &, int, int, bool, int64_t, int, \
                                          size_t, hipStream_t);                                \
-    extern template hipError_t dequantize_d<N>(const TensorDev &, int, float *, hipStream_t);
+    extern template hipError_t dequantize_d<N>(const TensorDev &, int, float *, hipStream_t); \
+    extern template hipError_t mix_d<N>(int, const MixArgs &, size_t, hipStream_t);
 VQ_DECL_D(2)
 VQ_DECL_D(4)
 VQ_DECL_D(8)
@@ -175,6 +176,72 @@ hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream)
     case 2: return rows_d<2>(t0.bits, a, gpl, L.nproj, L.act_f32 != 0, units, n_cu, lds, stream);
     case 4: return rows_d<4>(t0.bits, a, gpl, L.nproj, L.act_f32 != 0, units, n_cu, lds, stream);
     case 8: return rows_d<8>(t0.bits, a, gpl, L.nproj, L.act_f32 != 0, units, n_cu, lds, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// LDS of the fused down projection and combine (0: not applicable).
+static size_t mix_lds_bytes(const TensorDev &dn, int n_tok, int top_k, int &list_off, int &x_off,
+                            int &m_off, int &y_off)
+{
+    const int P = n_tok * top_k;
+    if (dn.groups > 64 || n_tok > 16 || P > kMaxSlots)
+        return 0;
+    int off = (dn.cb_dwords + 3) & ~3;
+    list_off = off;
+    off += (list_dwords(P) + 3) & ~3;
+    x_off = off;
+    off += P * dn.groups * kMixXStride;
+    m_off = off;
+    off += (P * dn.groups + 3) & ~3;
+    y_off = off;
+    off += kWaves * 64 * n_tok;
+    const size_t bytes = (size_t)off * 4;
+    return bytes <= 65536 ? bytes : 0;
+}
+
+bool mix_supported(const TensorDev &dn, int n_tok, int top_k)
+{
+    int l, x, m, y;
+    return mix_lds_bytes(dn, n_tok, top_k, l, x, m, y) != 0;
+}
+
+hipError_t launch_mix(const TensorDev &dn, int n_tok, int top_k, const float *h,
+                      const int32_t *ids, const float *w, float *y, hipStream_t stream)
+{
+    if (n_tok == 0 || dn.rows == 0)
+        return hipSuccess;
+    if (dn.n_stored == 0)
+        return launch_fill_rows(y, n_tok, dn.rows, dn.rows, stream);
+    MixArgs a = {};
+    const size_t lds = mix_lds_bytes(dn, n_tok, top_k, a.list_offset, a.x_offset, a.m_offset,
+                                     a.y_offset);
+    if (lds == 0)
+        return hipErrorInvalidValue;
+    int s_log2 = 0;
+    while ((1 << s_log2) < dn.groups)
+        ++s_log2;
+    a.codes = dn.codes;
+    a.scales = dn.scales;
+    a.row_map = dn.row_map;
+    a.codebook = dn.codebook;
+    a.cb_dwords = dn.cb_dwords;
+    a.rows = dn.rows;
+    a.groups = dn.groups;
+    a.wpr = dn.wpr;
+    a.S_log2 = s_log2;
+    a.h = h;
+    a.ids = ids;
+    a.w = w;
+    a.n_tok = n_tok;
+    a.top_k = top_k;
+    a.y = y;
+    const int rpw = 64 >> s_log2;
+    a.units = (dn.rows + rpw - 1) / rpw;
+    switch (dn.d) {
+    case 2: return mix_d<2>(dn.bits, a, lds, stream);
+    case 4: return mix_d<4>(dn.bits, a, lds, stream);
+    case 8: return mix_d<8>(dn.bits, a, lds, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -6,5 +6,6 @@ namespace vq {
 template hipError_t rows_d<4>(int, const RowsArgs &, int, int, bool, int64_t, int, size_t,
                                hipStream_t);
 template hipError_t dequantize_d<4>(const TensorDev &, int, float *, hipStream_t);
+template hipError_t mix_d<4>(int, const MixArgs &, size_t, hipStream_t);
 
 }  // namespace vq

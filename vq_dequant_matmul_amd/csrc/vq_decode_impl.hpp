@@ -423,6 +423,23 @@ __device__ __forceinline__ Lists lists_at(uint32_t *lds, int offset, int P)
 
 constexpr int list_dwords(int P) { return 7 * P + 2; }
 
+// Lists of a single token's pairs: one "distinct expert" per pair (a
+// repeated id is then simply streamed twice).  Called by every thread.
+__device__ __forceinline__ void single_token_lists(const Lists &L, const int32_t *ids, int P)
+{
+    for (int q = threadIdx.x; q < P; q += kThreads) {
+        const int id = ids[q];
+        L.ids[q] = id;
+        L.uexp[q] = id;
+        L.items[q] = q;
+        L.ustart[q] = q;
+    }
+    if (threadIdx.x == 0) {
+        L.ustart[P] = P;
+        *L.U = P;
+    }
+}
+
 // Called by every thread after L.ids is filled and a barrier.
 __device__ __forceinline__ void build_lists(const Lists &L, int P)
 {
@@ -502,7 +519,10 @@ __global__ __launch_bounds__(kThreads) void k_rows(const RowsArgs a)
     load_codebooks<D, BITS, NPROJ>(a, cr);
     const int P = a.ids ? a.n_slots : a.n_act;
     const Lists L = lists_at(lds, a.list_offset, P);
-    if (a.ids) {
+    const bool one_token = a.ids && a.act_div == a.n_slots;
+    if (one_token) {
+        single_token_lists(L, a.ids, P);
+    } else if (a.ids) {
         for (int q = tid; q < P; q += kThreads)
             L.ids[q] = a.ids[q];
     } else {
@@ -519,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void k_rows(const RowsArgs a)
     }
     store_codebooks<D, BITS, NPROJ>(a, cr, lds);
     __syncthreads();
-    if (a.ids)
+    if (a.ids && !one_token)
         build_lists(L, P);
 
     // ---- this workgroup's contiguous range of units (expert, tile, pair) -----
@@ -662,6 +682,218 @@ template <int D>
 hipError_t dequantize_d(const TensorDev &t, int e, float *w, hipStream_t s)
 {
     VQ_BITS_SWITCH(t.bits, DequantD<D>::template run, t, e, w, s)
+}
+
+// --------------------------------------------------------------------------------
+// down projection fused with the combine, for a few tokens, by output rows
+// --------------------------------------------------------------------------------
+// y[t][r] = sum over the (token, slot) pairs q of token t of
+// w[q] * (W_down_{e_q} h_q)[r], added in a fixed order (distinct experts in
+// first-occurrence order, then each expert's pairs in slot order).  A wave
+// owns rpw output rows (one per segment of S lanes, each lane one 64-column
+// group of the row, S >= groups) and walks the distinct routed experts: it
+// streams each expert's rows once, with the next expert's words in flight,
+// and applies them to every pair routed to that expert, adding the weighted
+// products into per-(row, token) sums in LDS.  h is converted once per
+// workgroup into range-scaled fp16 (a power of two per pair and group), the
+// same activation format as the gate and up projections.
+struct MixArgs {
+    const uint32_t *codes;
+    const uint16_t *scales;
+    const int32_t *row_map;
+    const uint16_t *codebook;
+    int cb_dwords;
+    int rows, groups, wpr;   // rows = hidden, groups = inter / 64
+    int S_log2;
+    const float *h;          // [P][inter]
+    const int32_t *ids;      // [P]
+    const float *w;          // [P]
+    int n_tok, top_k;
+    float *y;                // [n_tok][rows]
+    int list_offset, x_offset, m_offset, y_offset;   // LDS dword offsets
+    int units;               // tiles of rpw rows
+};
+
+constexpr int kMixXStride = 36;   // dwords per (pair, group): 32 used, padded for ds_read_b128
+constexpr int kMixChunk = 8;      // experts whose rows are loaded together
+
+template <int D, int BITS>
+__global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
+{
+    using GM = Geom<D, BITS>;
+    constexpr int NW = GM::NW;
+    constexpr int G = GM::G;
+    constexpr int HP = D / 2;
+    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int P = a.n_tok * a.top_k;
+
+    // ---- setup: codebook, routing lists, h as range-scaled fp16 pairs ------------
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.codebook);
+        const int n4 = a.cb_dwords >> 2;
+        for (int i = tid; i < n4; i += kThreads)
+            reinterpret_cast<uint4 *>(lds)[i] = src[i];
+        const uint32_t *s32 = reinterpret_cast<const uint32_t *>(a.codebook);
+        for (int i = (n4 << 2) + tid; i < a.cb_dwords; i += kThreads)
+            lds[i] = s32[i];
+    }
+    const Lists L = lists_at(lds, a.list_offset, P);
+    if (a.n_tok == 1)
+        single_token_lists(L, a.ids, P);
+    else
+        for (int q = tid; q < P; q += kThreads)
+            L.ids[q] = a.ids[q];
+    uint32_t *xs = lds + a.x_offset;                    // [P][groups][kMixXStride]
+    float *xm = reinterpret_cast<float *>(lds + a.m_offset);   // [P][groups]
+    for (int it = tid; it < P * a.groups; it += kThreads) {
+        const int q = it / a.groups;
+        const int g = it - q * a.groups;
+        const float4 *src = reinterpret_cast<const float4 *>(a.h + ((int64_t)q * a.groups + g) * 64);
+        float4 v[16];
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            v[j] = src[j];
+            amax = fmaxf(fmaxf(amax, fmaxf(fabsf(v[j].x), fabsf(v[j].y))),
+                         fmaxf(fabsf(v[j].z), fabsf(v[j].w)));
+        }
+        const int k = range_exponent(amax);
+        const float up = ldexpf(1.0f, k);
+        uint4 *dst = reinterpret_cast<uint4 *>(xs + (size_t)it * kMixXStride);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            union { f16x2 h[4]; uint4 u; } o;
+            o.h[0] = pack_f16x2(v[2 * j].x * up, v[2 * j].y * up);
+            o.h[1] = pack_f16x2(v[2 * j].z * up, v[2 * j].w * up);
+            o.h[2] = pack_f16x2(v[2 * j + 1].x * up, v[2 * j + 1].y * up);
+            o.h[3] = pack_f16x2(v[2 * j + 1].z * up, v[2 * j + 1].w * up);
+            dst[j] = o.u;
+        }
+        xm[it] = ldexpf(1.0f, -k);
+    }
+    __syncthreads();
+    if (a.n_tok != 1)
+        build_lists(L, P);
+
+    // ---- output row tiles, one per wave at a time ---------------------------------
+    const int S = 1 << a.S_log2;
+    const int rpw = 64 >> a.S_log2;
+    const int seg = lane >> a.S_log2;
+    const int sl = lane & (S - 1);
+    const int g = min(sl, a.groups - 1);
+    const bool gok = sl < a.groups;
+    float *yacc = reinterpret_cast<float *>(lds + a.y_offset) + wave * 64 * a.n_tok;
+    const int U = *L.U;
+    for (int unit = blockIdx.x * kWaves + wave; unit < a.units; unit += gridDim.x * kWaves) {
+        const int r = unit * rpw + seg;
+        const bool rok = r < a.rows;
+        for (int t = sl; t < a.n_tok; t += S)
+            yacc[seg * a.n_tok + t] = 0.0f;
+        // the words of up to kMixChunk experts are loaded together, so their
+        // memory latencies overlap
+        for (int u0 = 0; u0 < U; u0 += kMixChunk) {
+            uint32_t wd[kMixChunk][NW];
+            uint32_t sc[kMixChunk];
+            int live = 0;
+            // every load unconditional (entries past U repeat the last
+            // expert and are skipped below)
+            int64_t srow[kMixChunk];
+#pragma unroll
+            for (int c = 0; c < kMixChunk; ++c) {
+                const int64_t lin =
+                    (int64_t)L.uexp[min(u0 + c, U - 1)] * a.rows + min(r, a.rows - 1);
+                srow[c] = a.row_map ? a.row_map[lin] : lin;
+            }
+#pragma unroll
+            for (int c = 0; c < kMixChunk; ++c) {
+                const bool lv = rok && (srow[c] >= 0);
+                live |= lv ? (1 << c) : 0;
+                const int64_t sr = lv ? srow[c] : 0;
+                const uint32_t *row = a.codes + sr * a.wpr;
+                const int w0 = (g * GM::GB) >> 5;
+                if constexpr (GM::CLAMP) {
+#pragma unroll
+                    for (int k = 0; k < NW; ++k)
+                        wd[c][k] = row[min(w0 + k, a.wpr - 1)];
+                } else {
+                    __builtin_memcpy(wd[c], row + w0, NW * 4);
+                }
+                sc[c] = a.scales[sr * a.groups + g];
+            }
+#pragma unroll
+            for (int c = 0; c < kMixChunk; ++c) {
+                if (u0 + c >= U)
+                    break;
+                const int u = u0 + c;
+                uint32_t nw[NW];
+                shift_group_words<D, BITS>(g, wd[c], nw);
+                const bool lv = (live >> c) & 1;
+                const float sf = (lv && gok) ? half_bits_to_float(sc[c]) : 0.0f;
+                for (int i = L.ustart[u]; i < L.ustart[u + 1]; ++i) {
+                    const int q = L.items[i];
+                    const uint4 *xp =
+                        reinterpret_cast<const uint4 *>(xs + (size_t)(q * a.groups + g) * kMixXStride);
+                    union { uint4 u[8]; f16x2 h[32]; } x;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        x.u[j] = xp[j];
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int t = 0; t < G; ++t) {
+                        const uint32_t code = extract<BITS, NW>(nw, t);
+                        const Entry<D> en = fetch_entry<D>(lds, code);
+#pragma unroll
+                        for (int k = 0; k < HP; ++k)
+                            acc = dot2(en.v[k], x.h[t * HP + k], acc);
+                    }
+                    float part = acc * (sf * xm[q * a.groups + g]);
+#pragma unroll
+                    for (int m = 32; m >= 1; m >>= 1)
+                        if (m < S)
+                            part += __shfl_xor(part, m, 64);
+                    if (sl == 0 && lv)
+                        yacc[seg * a.n_tok + q / a.top_k] += a.w[q] * part;
+                }
+            }
+        }
+        if (rok)
+            for (int t = sl; t < a.n_tok; t += S)
+                a.y[(int64_t)t * a.rows + r] = yacc[seg * a.n_tok + t];
+    }
+}
+
+template <int D, int BITS>
+static hipError_t mix_db(const MixArgs &a, size_t lds, hipStream_t stream)
+{
+    auto kern = k_mix<D, BITS>;
+    if (lds > 65536) {
+        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (err != hipSuccess)
+            return err;
+    }
+    const int wgs = (a.units + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(wgs < 1024 ? wgs : 1024)), dim3(kThreads), lds, stream,
+                       a);
+    return hipGetLastError();
+}
+
+template <int D>
+struct MixD {
+    template <int BITS>
+    static hipError_t run(const MixArgs &a, size_t lds, hipStream_t s)
+    {
+        return mix_db<D, BITS>(a, lds, s);
+    }
+};
+
+template <int D>
+hipError_t mix_d(int bits, const MixArgs &a, size_t lds, hipStream_t s)
+{
+    VQ_BITS_SWITCH(bits, MixD<D>::template run, a, lds, s)
 }
 
 constexpr int kIters = 2;

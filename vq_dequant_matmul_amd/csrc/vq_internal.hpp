@@ -55,6 +55,13 @@ hipError_t launch_combine(const float *z, const float *w, int n_tok, int top_k, 
 
 hipError_t launch_dequantize(const TensorDev &t, int expert, float *w, hipStream_t stream);
 
+// Down projection fused with the slot-ordered combine for a few tokens:
+// y[t] = sum_s w[t][s] * W_down_{e[t][s]} h[t*top_k + s].  mix_supported()
+// tells whether the shapes fit the fused kernel.
+bool mix_supported(const TensorDev &dn, int n_tok, int top_k);
+hipError_t launch_mix(const TensorDev &dn, int n_tok, int top_k, const float *h,
+                      const int32_t *ids, const float *w, float *y, hipStream_t stream);
+
 // Prefill (MFMA) path.
 struct GemmLaunch;
 size_t gemm_workspace_bytes(const TensorDev &t, int n_x_rows);

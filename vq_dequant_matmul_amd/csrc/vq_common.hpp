@@ -183,22 +183,32 @@ __device__ __forceinline__ float dot2(uint32_t cb_pair, f16x2 x, float acc)
 
 // ---- wavefront helpers ------------------------------------------------------
 
-// Sum over aligned segments of S lanes (S a power of two <= 64).
-template <int S>
-__device__ __forceinline__ float segment_sum(float v)
+// v combined with lane (l ^ 1), (l ^ 2) (quad permutations), then across
+// the halves of each 8-lane group and of each 16-lane row (half-mirror and
+// mirror): DPP moves, so no LDS traffic.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v)
 {
-#pragma unroll
-    for (int m = S / 2; m >= 1; m >>= 1)
-        v += __shfl_xor(v, m, 64);
-    return v;
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
 }
 
-template <int S>
-__device__ __forceinline__ float segment_max(float v)
+// Sum over aligned segments of S lanes (S a power of two <= 64, uniform);
+// every lane of a segment receives the segment's sum.  Steps inside a
+// 16-lane row use DPP, wider ones a cross-lane permute.
+__device__ __forceinline__ float segment_sum_dpp(float v, int S)
 {
-#pragma unroll
-    for (int m = S / 2; m >= 1; m >>= 1)
-        v = fmaxf(v, __shfl_xor(v, m, 64));
+    if (S >= 2)
+        v += dpp_move<0xb1>(v);    // quad_perm [1,0,3,2]
+    if (S >= 4)
+        v += dpp_move<0x4e>(v);    // quad_perm [2,3,0,1]
+    if (S >= 8)
+        v += dpp_move<0x141>(v);   // row_half_mirror
+    if (S >= 16)
+        v += dpp_move<0x140>(v);   // row_mirror
+    if (S >= 32)
+        v += __shfl_xor(v, 16, 64);
+    if (S >= 64)
+        v += __shfl_xor(v, 32, 64);
     return v;
 }
 

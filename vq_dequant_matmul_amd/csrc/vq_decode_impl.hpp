@@ -311,16 +311,10 @@ __device__ __forceinline__ void compute_rows(const RowsArgs &a, const uint32_t *
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // segment butterfly (S is uniform)
+        // segment reduction (S is uniform)
 #pragma unroll
-        for (int p = 0; p < NPROJ; ++p) {
-            float v = part[p];
-#pragma unroll
-            for (int m = 32; m >= 1; m >>= 1)
-                if (m < S)
-                    v += __shfl_xor(v, m, 64);
-            part[p] = v;
-        }
+        for (int p = 0; p < NPROJ; ++p)
+            part[p] = segment_sum_dpp(part[p], S);
         if (sl == 0 && r < a.rows) {
             float val;
             if constexpr (NPROJ == 2)
@@ -514,12 +508,43 @@ __global__ __launch_bounds__(kThreads) void k_rows(const RowsArgs a)
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
+    // ---- this workgroup's contiguous range of units (expert, tile, pair) -----
+    const int P = a.ids ? a.n_slots : a.n_act;
+    const bool one_token = a.ids && a.act_div == a.n_slots;
+    const int S = 1 << a.S_log2;
+    const int rpw = 64 >> a.S_log2;
+    const int seg = lane >> a.S_log2;
+    const int sl = lane & (S - 1);
+    const int64_t n_units = (int64_t)P * a.tiles;
+    int64_t k = (int64_t)blockIdx.x * n_units / gridDim.x;
+    const int64_t k_end = (int64_t)(blockIdx.x + 1) * n_units / gridDim.x;
+    struct Unit {
+        int item, e, row0;
+    };
+    // With one expert, or one token's pairs, a unit's expert is known without
+    // the lists: its rows are requested before the setup below, so that the
+    // memory latency overlaps the codebook staging.
+    RowRegs<D, BITS, GPL, NPROJ> A[ITERS], B[ITERS];
+    Unit ua, ub;
+    const bool direct = one_token || !a.ids;
+    if (direct && k < k_end) {
+        if (one_token) {
+            ua.item = (int)(k / a.tiles);
+            ua.e = a.ids[ua.item];
+            ua.row0 = (int)(k - (int64_t)ua.item * a.tiles) * a.tile_rows + wave * ITERS * rpw;
+        } else {
+            const int t = (int)(k / P);
+            ua.item = (int)(k - (int64_t)t * P);
+            ua.e = a.expert;
+            ua.row0 = t * a.tile_rows + wave * ITERS * rpw;
+        }
+        load_rows<D, BITS, GPL, NPROJ, ITERS>(a, ua.e, ua.row0, rpw, seg, sl, S, A);
+    }
+
     // ---- setup: codebooks and work lists, once per workgroup -----------------
     CbRegs<D, BITS, NPROJ> cr;
     load_codebooks<D, BITS, NPROJ>(a, cr);
-    const int P = a.ids ? a.n_slots : a.n_act;
     const Lists L = lists_at(lds, a.list_offset, P);
-    const bool one_token = a.ids && a.act_div == a.n_slots;
     if (one_token) {
         single_token_lists(L, a.ids, P);
     } else if (a.ids) {
@@ -542,19 +567,8 @@ __global__ __launch_bounds__(kThreads) void k_rows(const RowsArgs a)
     if (a.ids && !one_token)
         build_lists(L, P);
 
-    // ---- this workgroup's contiguous range of units (expert, tile, pair) -----
-    const int S = 1 << a.S_log2;
-    const int rpw = 64 >> a.S_log2;
-    const int seg = lane >> a.S_log2;
-    const int sl = lane & (S - 1);
-    const int64_t n_units = (int64_t)P * a.tiles;
-    int64_t k = (int64_t)blockIdx.x * n_units / gridDim.x;
-    const int64_t k_end = (int64_t)(blockIdx.x + 1) * n_units / gridDim.x;
     // Units are software-pipelined two deep: the rows of unit k+1 are in
     // flight while unit k is computed (buffers A and B alternate).
-    struct Unit {
-        int item, e, row0;
-    };
     int u = 0;
     auto unit_at = [&](int64_t kk) {
         while (kk >= (int64_t)L.ustart[u + 1] * a.tiles)
@@ -583,9 +597,10 @@ __global__ __launch_bounds__(kThreads) void k_rows(const RowsArgs a)
     };
     if (k >= k_end)
         return;
-    RowRegs<D, BITS, GPL, NPROJ> A[ITERS], B[ITERS];
-    Unit ua = unit_at(k), ub;
-    load_rows<D, BITS, GPL, NPROJ, ITERS>(a, ua.e, ua.row0, rpw, seg, sl, S, A);
+    if (!direct) {
+        ua = unit_at(k);
+        load_rows<D, BITS, GPL, NPROJ, ITERS>(a, ua.e, ua.row0, rpw, seg, sl, S, A);
+    }
     for (;;) {
         const bool more_b = k + 1 < k_end;
         if (more_b) {
@@ -730,6 +745,65 @@ __global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
     const int wave = tid >> 6;
     const int P = a.n_tok * a.top_k;
 
+    // ---- per-lane constants; the rows of a single token's experts are
+    // requested before the setup below, so that their memory latency
+    // overlaps it -------------------------------------------------------------------
+    const int S = 1 << a.S_log2;
+    const int rpw = 64 >> a.S_log2;
+    const int seg = lane >> a.S_log2;
+    const int sl = lane & (S - 1);
+    const int g = min(sl, a.groups - 1);
+    const bool gok = sl < a.groups;
+    const bool one = a.n_tok == 1;
+    const Lists L = lists_at(lds, a.list_offset, P);
+    // the words of up to kMixChunk experts are loaded together, so their
+    // memory latencies overlap; every load is unconditional (entries past U
+    // repeat the last expert and are skipped)
+    uint32_t wd[kMixChunk][NW];
+    uint32_t sc[kMixChunk];
+    int live = 0;
+    auto load_chunk = [&](int r, int u0, int u_end) {
+        const bool rok = r < a.rows;
+        int64_t srow[kMixChunk];
+#pragma unroll
+        for (int c = 0; c < kMixChunk; ++c) {
+            const int u = min(u0 + c, u_end - 1);
+            const int e = one ? a.ids[u] : L.uexp[u];
+            const int64_t lin = (int64_t)e * a.rows + min(r, a.rows - 1);
+            srow[c] = a.row_map ? a.row_map[lin] : lin;
+        }
+        live = 0;
+#pragma unroll
+        for (int c = 0; c < kMixChunk; ++c) {
+            const bool lv = rok && (srow[c] >= 0);
+            live |= lv ? (1 << c) : 0;
+            const int64_t sr = lv ? srow[c] : 0;
+            const uint32_t *row = a.codes + sr * a.wpr;
+            const int w0 = (g * GM::GB) >> 5;
+            if constexpr (GM::CLAMP) {
+#pragma unroll
+                for (int k = 0; k < NW; ++k)
+                    wd[c][k] = row[min(w0 + k, a.wpr - 1)];
+            } else {
+                __builtin_memcpy(wd[c], row + w0, NW * 4);
+            }
+            sc[c] = a.scales[sr * a.groups + g];
+        }
+    };
+    // a workgroup owns a tile of rpw output rows; its waves split the
+    // distinct experts into contiguous ranges
+    const int unit0 = blockIdx.x;
+    auto wave_range = [&](int U, int &ub, int &ue) {
+        const int per = (U + kWaves - 1) / kWaves;
+        ub = min(wave * per, U);
+        ue = min(ub + per, U);
+    };
+    int ub0, ue0;
+    wave_range(P, ub0, ue0);
+    const bool preloaded = one && unit0 < a.units && ub0 < ue0;
+    if (preloaded)
+        load_chunk(unit0 * rpw + seg, ub0, ue0);
+
     // ---- setup: codebook, routing lists, h as range-scaled fp16 pairs ------------
     {
         const uint4 *src = reinterpret_cast<const uint4 *>(a.codebook);
@@ -740,7 +814,6 @@ __global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
         for (int i = (n4 << 2) + tid; i < a.cb_dwords; i += kThreads)
             lds[i] = s32[i];
     }
-    const Lists L = lists_at(lds, a.list_offset, P);
     if (a.n_tok == 1)
         single_token_lists(L, a.ids, P);
     else
@@ -750,8 +823,8 @@ __global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
     float *xm = reinterpret_cast<float *>(lds + a.m_offset);   // [P][groups]
     for (int it = tid; it < P * a.groups; it += kThreads) {
         const int q = it / a.groups;
-        const int g = it - q * a.groups;
-        const float4 *src = reinterpret_cast<const float4 *>(a.h + ((int64_t)q * a.groups + g) * 64);
+        const int gg = it - q * a.groups;
+        const float4 *src = reinterpret_cast<const float4 *>(a.h + ((int64_t)q * a.groups + gg) * 64);
         float4 v[16];
         float amax = 0.0f;
 #pragma unroll
@@ -778,54 +851,24 @@ __global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
     if (a.n_tok != 1)
         build_lists(L, P);
 
-    // ---- output row tiles, one per wave at a time ---------------------------------
-    const int S = 1 << a.S_log2;
-    const int rpw = 64 >> a.S_log2;
-    const int seg = lane >> a.S_log2;
-    const int sl = lane & (S - 1);
-    const int g = min(sl, a.groups - 1);
-    const bool gok = sl < a.groups;
-    float *yacc = reinterpret_cast<float *>(lds + a.y_offset) + wave * 64 * a.n_tok;
+    // ---- output row tiles, one per workgroup at a time ----------------------------
+    // yacc[w][row][t]: wave w's partial sums; added in wave order at the end
+    float *yall = reinterpret_cast<float *>(lds + a.y_offset);
+    float *yacc = yall + wave * 64 * a.n_tok;
     const int U = *L.U;
-    for (int unit = blockIdx.x * kWaves + wave; unit < a.units; unit += gridDim.x * kWaves) {
+    int ub, ue;
+    wave_range(U, ub, ue);
+    for (int unit = unit0; unit < a.units; unit += gridDim.x) {
         const int r = unit * rpw + seg;
         const bool rok = r < a.rows;
         for (int t = sl; t < a.n_tok; t += S)
             yacc[seg * a.n_tok + t] = 0.0f;
-        // the words of up to kMixChunk experts are loaded together, so their
-        // memory latencies overlap
-        for (int u0 = 0; u0 < U; u0 += kMixChunk) {
-            uint32_t wd[kMixChunk][NW];
-            uint32_t sc[kMixChunk];
-            int live = 0;
-            // every load unconditional (entries past U repeat the last
-            // expert and are skipped below)
-            int64_t srow[kMixChunk];
+        for (int u0 = ub; u0 < ue; u0 += kMixChunk) {
+            if (!(preloaded && unit == unit0 && u0 == ub))
+                load_chunk(r, u0, ue);
 #pragma unroll
             for (int c = 0; c < kMixChunk; ++c) {
-                const int64_t lin =
-                    (int64_t)L.uexp[min(u0 + c, U - 1)] * a.rows + min(r, a.rows - 1);
-                srow[c] = a.row_map ? a.row_map[lin] : lin;
-            }
-#pragma unroll
-            for (int c = 0; c < kMixChunk; ++c) {
-                const bool lv = rok && (srow[c] >= 0);
-                live |= lv ? (1 << c) : 0;
-                const int64_t sr = lv ? srow[c] : 0;
-                const uint32_t *row = a.codes + sr * a.wpr;
-                const int w0 = (g * GM::GB) >> 5;
-                if constexpr (GM::CLAMP) {
-#pragma unroll
-                    for (int k = 0; k < NW; ++k)
-                        wd[c][k] = row[min(w0 + k, a.wpr - 1)];
-                } else {
-                    __builtin_memcpy(wd[c], row + w0, NW * 4);
-                }
-                sc[c] = a.scales[sr * a.groups + g];
-            }
-#pragma unroll
-            for (int c = 0; c < kMixChunk; ++c) {
-                if (u0 + c >= U)
+                if (u0 + c >= ue)
                     break;
                 const int u = u0 + c;
                 uint32_t nw[NW];
@@ -849,19 +892,25 @@ __global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
                         for (int k = 0; k < HP; ++k)
                             acc = dot2(en.v[k], x.h[t * HP + k], acc);
                     }
-                    float part = acc * (sf * xm[q * a.groups + g]);
-#pragma unroll
-                    for (int m = 32; m >= 1; m >>= 1)
-                        if (m < S)
-                            part += __shfl_xor(part, m, 64);
+                    const float part = segment_sum_dpp(acc * (sf * xm[q * a.groups + g]), S);
                     if (sl == 0 && lv)
                         yacc[seg * a.n_tok + q / a.top_k] += a.w[q] * part;
                 }
             }
         }
-        if (rok)
-            for (int t = sl; t < a.n_tok; t += S)
-                a.y[(int64_t)t * a.rows + r] = yacc[seg * a.n_tok + t];
+        __syncthreads();
+        // wave order fixes the order of the sums
+        for (int i = tid; i < rpw * a.n_tok; i += kThreads) {
+            const int rr = unit * rpw + i / a.n_tok;
+            const int t = i - (i / a.n_tok) * a.n_tok;
+            float v = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w)
+                v += yall[w * 64 * a.n_tok + i];
+            if (rr < a.rows)
+                a.y[(int64_t)t * a.rows + rr] = v;
+        }
+        __syncthreads();
     }
 }
 
@@ -875,9 +924,8 @@ static hipError_t mix_db(const MixArgs &a, size_t lds, hipStream_t stream)
         if (err != hipSuccess)
             return err;
     }
-    const int wgs = (a.units + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(wgs < 1024 ? wgs : 1024)), dim3(kThreads), lds, stream,
-                       a);
+    const int wgs = a.units < 2048 ? a.units : 2048;
+    hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
 }
 

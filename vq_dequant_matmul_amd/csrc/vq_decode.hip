@@ -238,6 +238,7 @@ hipError_t launch_mix(const TensorDev &dn, int n_tok, int top_k, const float *h,
     a.y = y;
     const int rpw = 64 >> s_log2;
     a.units = (dn.rows + rpw - 1) / rpw;
+    a.max_wgs = 2 * cu_count();
     switch (dn.d) {
     case 2: return mix_d<2>(dn.bits, a, lds, stream);
     case 4: return mix_d<4>(dn.bits, a, lds, stream);

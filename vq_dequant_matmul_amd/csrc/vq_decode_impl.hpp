@@ -727,10 +727,11 @@ struct MixArgs {
     float *y;                // [n_tok][rows]
     int list_offset, x_offset, m_offset, y_offset;   // LDS dword offsets
     int units;               // tiles of rpw rows
+    int max_wgs;             // grid cap (a few workgroups per CU)
 };
 
 constexpr int kMixXStride = 36;   // dwords per (pair, group): 32 used, padded for ds_read_b128
-constexpr int kMixChunk = 8;      // experts whose rows are loaded together
+constexpr int kMixChunk = 4;      // experts whose rows are loaded together
 
 template <int D, int BITS>
 __global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
@@ -745,9 +746,6 @@ __global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
     const int wave = tid >> 6;
     const int P = a.n_tok * a.top_k;
 
-    // ---- per-lane constants; the rows of a single token's experts are
-    // requested before the setup below, so that their memory latency
-    // overlaps it -------------------------------------------------------------------
     const int S = 1 << a.S_log2;
     const int rpw = 64 >> a.S_log2;
     const int seg = lane >> a.S_log2;
@@ -756,53 +754,70 @@ __global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
     const bool gok = sl < a.groups;
     const bool one = a.n_tok == 1;
     const Lists L = lists_at(lds, a.list_offset, P);
-    // the words of up to kMixChunk experts are loaded together, so their
-    // memory latencies overlap; every load is unconditional (entries past U
-    // repeat the last expert and are skipped)
-    uint32_t wd[kMixChunk][NW];
-    uint32_t sc[kMixChunk];
-    int live = 0;
-    auto load_chunk = [&](int r, int u0, int u_end) {
+
+    // A workgroup walks tiles of rpw output rows (blockIdx.x, + gridDim.x,
+    // ...); its waves split the distinct experts into contiguous ranges of
+    // at most per = ceil(U / waves), taken kMixChunk at a time.  Work item i
+    // of a wave is (tile i / nch, chunk i % nch); the words of item i+1 are
+    // in flight while item i is computed.  For a single token the experts
+    // are the ids themselves, so the first item is requested before the
+    // setup below and its memory latency overlaps it.
+    struct Chunk {
+        uint32_t wd[kMixChunk][NW];
+        uint32_t sc[kMixChunk];
+        int live;
+    };
+    auto wave_range = [&](int U, int &ub, int &ue, int &nch) {
+        const int per = (U + kWaves - 1) / kWaves;
+        ub = min(wave * per, U);
+        ue = min(ub + per, U);
+        nch = max(1, (per + kMixChunk - 1) / kMixChunk);   // the same for every wave
+    };
+    const int my_units =
+        (int)blockIdx.x < a.units ? (a.units - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+    // every load unconditional (entries past the range repeat its last
+    // expert and are skipped)
+    auto load_item = [&](Chunk &ck, int item, int ub, int ue, int nch) {
+        const int unit = blockIdx.x + (item / nch) * gridDim.x;
+        const int u0 = ub + (item % nch) * kMixChunk;
+        const int r = unit * rpw + seg;
         const bool rok = r < a.rows;
         int64_t srow[kMixChunk];
 #pragma unroll
         for (int c = 0; c < kMixChunk; ++c) {
-            const int u = min(u0 + c, u_end - 1);
+            const int u = max(min(u0 + c, ue - 1), 0);
             const int e = one ? a.ids[u] : L.uexp[u];
             const int64_t lin = (int64_t)e * a.rows + min(r, a.rows - 1);
             srow[c] = a.row_map ? a.row_map[lin] : lin;
         }
-        live = 0;
+        ck.live = 0;
 #pragma unroll
         for (int c = 0; c < kMixChunk; ++c) {
             const bool lv = rok && (srow[c] >= 0);
-            live |= lv ? (1 << c) : 0;
+            ck.live |= lv ? (1 << c) : 0;
             const int64_t sr = lv ? srow[c] : 0;
             const uint32_t *row = a.codes + sr * a.wpr;
             const int w0 = (g * GM::GB) >> 5;
             if constexpr (GM::CLAMP) {
 #pragma unroll
                 for (int k = 0; k < NW; ++k)
-                    wd[c][k] = row[min(w0 + k, a.wpr - 1)];
+                    ck.wd[c][k] = row[min(w0 + k, a.wpr - 1)];
             } else {
-                __builtin_memcpy(wd[c], row + w0, NW * 4);
+                __builtin_memcpy(ck.wd[c], row + w0, NW * 4);
             }
-            sc[c] = a.scales[sr * a.groups + g];
+            ck.sc[c] = a.scales[sr * a.groups + g];
         }
     };
-    // a workgroup owns a tile of rpw output rows; its waves split the
-    // distinct experts into contiguous ranges
-    const int unit0 = blockIdx.x;
-    auto wave_range = [&](int U, int &ub, int &ue) {
-        const int per = (U + kWaves - 1) / kWaves;
-        ub = min(wave * per, U);
-        ue = min(ub + per, U);
-    };
-    int ub0, ue0;
-    wave_range(P, ub0, ue0);
-    const bool preloaded = one && unit0 < a.units && ub0 < ue0;
-    if (preloaded)
-        load_chunk(unit0 * rpw + seg, ub0, ue0);
+    Chunk ca, cb;
+    int ub, ue, nch;
+    bool preloaded = false;
+    if (one) {
+        wave_range(P, ub, ue, nch);
+        if (my_units > 0) {
+            load_item(ca, 0, ub, ue, nch);
+            preloaded = true;
+        }
+    }
 
     // ---- setup: codebook, routing lists, h as range-scaled fp16 pairs ------------
     {
@@ -814,7 +829,7 @@ __global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
         for (int i = (n4 << 2) + tid; i < a.cb_dwords; i += kThreads)
             lds[i] = s32[i];
     }
-    if (a.n_tok == 1)
+    if (one)
         single_token_lists(L, a.ids, P);
     else
         for (int q = tid; q < P; q += kThreads)
@@ -848,69 +863,86 @@ __global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
         xm[it] = ldexpf(1.0f, -k);
     }
     __syncthreads();
-    if (a.n_tok != 1)
+    if (!one)
         build_lists(L, P);
+    const int U = *L.U;
+    if (!one)
+        wave_range(U, ub, ue, nch);
 
-    // ---- output row tiles, one per workgroup at a time ----------------------------
-    // yacc[w][row][t]: wave w's partial sums; added in wave order at the end
+    // ---- the work items ----------------------------------------------------------------
+    // yacc[w][row][t]: wave w's partial sums of the current tile, added in
+    // wave order when the tile is done
     float *yall = reinterpret_cast<float *>(lds + a.y_offset);
     float *yacc = yall + wave * 64 * a.n_tok;
-    const int U = *L.U;
-    int ub, ue;
-    wave_range(U, ub, ue);
-    for (int unit = unit0; unit < a.units; unit += gridDim.x) {
-        const int r = unit * rpw + seg;
-        const bool rok = r < a.rows;
-        for (int t = sl; t < a.n_tok; t += S)
-            yacc[seg * a.n_tok + t] = 0.0f;
-        for (int u0 = ub; u0 < ue; u0 += kMixChunk) {
-            if (!(preloaded && unit == unit0 && u0 == ub))
-                load_chunk(r, u0, ue);
+    const int n_items = my_units * nch;
+    auto process = [&](const Chunk &ck, int item) {
+        const int tile = item / nch;
+        const int ch = item - tile * nch;
+        const int unit = blockIdx.x + tile * gridDim.x;
+        const int u0 = ub + ch * kMixChunk;
+        if (ch == 0)
+            for (int t = sl; t < a.n_tok; t += S)
+                yacc[seg * a.n_tok + t] = 0.0f;
 #pragma unroll
-            for (int c = 0; c < kMixChunk; ++c) {
-                if (u0 + c >= ue)
-                    break;
-                const int u = u0 + c;
-                uint32_t nw[NW];
-                shift_group_words<D, BITS>(g, wd[c], nw);
-                const bool lv = (live >> c) & 1;
-                const float sf = (lv && gok) ? half_bits_to_float(sc[c]) : 0.0f;
-                for (int i = L.ustart[u]; i < L.ustart[u + 1]; ++i) {
-                    const int q = L.items[i];
-                    const uint4 *xp =
-                        reinterpret_cast<const uint4 *>(xs + (size_t)(q * a.groups + g) * kMixXStride);
-                    union { uint4 u[8]; f16x2 h[32]; } x;
+        for (int c = 0; c < kMixChunk; ++c) {
+            if (u0 + c >= ue)
+                break;
+            const int u = u0 + c;
+            uint32_t nw[NW];
+            shift_group_words<D, BITS>(g, ck.wd[c], nw);
+            const bool lv = (ck.live >> c) & 1;
+            const float sf = (lv && gok) ? half_bits_to_float(ck.sc[c]) : 0.0f;
+            for (int i = L.ustart[u]; i < L.ustart[u + 1]; ++i) {
+                const int q = L.items[i];
+                const uint4 *xp =
+                    reinterpret_cast<const uint4 *>(xs + (size_t)(q * a.groups + g) * kMixXStride);
+                union { uint4 u[8]; f16x2 h[32]; } x;
 #pragma unroll
-                    for (int j = 0; j < 8; ++j)
-                        x.u[j] = xp[j];
-                    float acc = 0.0f;
+                for (int j = 0; j < 8; ++j)
+                    x.u[j] = xp[j];
+                float acc = 0.0f;
 #pragma unroll
-                    for (int t = 0; t < G; ++t) {
-                        const uint32_t code = extract<BITS, NW>(nw, t);
-                        const Entry<D> en = fetch_entry<D>(lds, code);
+                for (int t = 0; t < G; ++t) {
+                    const uint32_t code = extract<BITS, NW>(nw, t);
+                    const Entry<D> en = fetch_entry<D>(lds, code);
 #pragma unroll
-                        for (int k = 0; k < HP; ++k)
-                            acc = dot2(en.v[k], x.h[t * HP + k], acc);
-                    }
-                    const float part = segment_sum_dpp(acc * (sf * xm[q * a.groups + g]), S);
-                    if (sl == 0 && lv)
-                        yacc[seg * a.n_tok + q / a.top_k] += a.w[q] * part;
+                    for (int k = 0; k < HP; ++k)
+                        acc = dot2(en.v[k], x.h[t * HP + k], acc);
                 }
+                const float part = segment_sum_dpp(acc * (sf * xm[q * a.groups + g]), S);
+                if (sl == 0 && lv)
+                    yacc[seg * a.n_tok + q / a.top_k] += a.w[q] * part;
             }
         }
-        __syncthreads();
-        // wave order fixes the order of the sums
-        for (int i = tid; i < rpw * a.n_tok; i += kThreads) {
-            const int rr = unit * rpw + i / a.n_tok;
-            const int t = i - (i / a.n_tok) * a.n_tok;
-            float v = 0.0f;
+        if (ch == nch - 1) {
+            __syncthreads();
+            // wave order fixes the order of the sums
+            for (int i = tid; i < rpw * a.n_tok; i += kThreads) {
+                const int rr = unit * rpw + i / a.n_tok;
+                const int t = i - (i / a.n_tok) * a.n_tok;
+                float v = 0.0f;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w)
-                v += yall[w * 64 * a.n_tok + i];
-            if (rr < a.rows)
-                a.y[(int64_t)t * a.rows + rr] = v;
+                for (int w = 0; w < kWaves; ++w)
+                    v += yall[w * 64 * a.n_tok + i];
+                if (rr < a.rows)
+                    a.y[(int64_t)t * a.rows + rr] = v;
+            }
+            __syncthreads();
         }
-        __syncthreads();
+    };
+    if (n_items == 0)
+        return;
+    if (!preloaded)
+        load_item(ca, 0, ub, ue, nch);
+    for (int i = 0; i < n_items; i += 2) {
+        if (i + 1 < n_items)
+            load_item(cb, i + 1, ub, ue, nch);
+        process(ca, i);
+        if (i + 1 >= n_items)
+            break;
+        if (i + 2 < n_items)
+            load_item(ca, i + 2, ub, ue, nch);
+        process(cb, i + 1);
     }
 }
 
@@ -924,7 +956,8 @@ static hipError_t mix_db(const MixArgs &a, size_t lds, hipStream_t stream)
         if (err != hipSuccess)
             return err;
     }
-    const int wgs = a.units < 2048 ? a.units : 2048;
+    // a few tiles per workgroup amortise staging h
+    const int wgs = a.units < a.max_wgs ? a.units : a.max_wgs;
     hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
 }

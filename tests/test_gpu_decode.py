@@ -191,3 +191,90 @@ def test_moe_decode_deterministic():
     a = _run_moe(gate, up, down, x, ids, w)
     b = _run_moe(gate, up, down, x, ids, w)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# one token
+# --------------------------------------------------------------------------
+
+def _one_token_layer(E=16, H=2048, I=768, d=4, bits=9, dead=0, seed=70, down_bits=None):
+    gate = synth.make_tensor(seed, 1, rows=I, cols=H, d=d, bits=bits, n_experts=E, dead_rows=dead)
+    up = synth.make_tensor(seed, 2, rows=I, cols=H, d=d, bits=bits, n_experts=E, dead_rows=dead)
+    down = synth.make_tensor(seed, 3, rows=H, cols=I, d=d, bits=down_bits or bits, n_experts=E,
+                             dead_rows=dead)
+    return gate, up, down
+
+
+def test_moe_decode_one_token_workspace_reuse():
+    """Consecutive one-token calls on one workspace: every output matches
+    the oracle (nothing carries over from the previous call)."""
+    E, k, H, I = 16, 8, 2048, 768
+    gate, up, down = _one_token_layer(E, H, I)
+    G, U, D = _dev(gate), _dev(up), _dev(down)
+    wl = synth.MoEWorkload("one", E, k, H, I, 4, 9, 1, seed=71)
+    ws = torch.empty(vq.vq_moe_ffn_workspace_size(G, U, D, 1, k), dtype=torch.uint8, device="cuda")
+    for step in range(6):
+        x, ids, w = synth.make_moe_inputs(wl, step)
+        y = vq.vq_moe_ffn(G, U, D, x_to_torch(x), torch.from_numpy(ids).cuda(),
+                          torch.from_numpy(w).cuda(), workspace=ws)
+        check_close(y.cpu().numpy(), oracle.moe_ffn(gate, up, down, x, ids, w), f"step {step}")
+
+
+@pytest.mark.parametrize("case", ["f32_x", "skip_zero", "repeated_id", "top1", "d2k1024_gpl2",
+                                  "mixed_bits"])
+def test_moe_decode_one_token_variants(case):
+    E, k, H, I, d, bits, dead, down_bits, dt = 12, 4, 1024, 512, 4, 9, 0, None, "bf16"
+    if case == "f32_x":
+        dt = "f32"
+    elif case == "skip_zero":
+        dead = 40
+    elif case == "top1":
+        k = 1
+    elif case == "d2k1024_gpl2":
+        H, d, bits = 8192, 2, 10
+    elif case == "mixed_bits":
+        down_bits = 8
+        d = 2
+    gate, up, down = _one_token_layer(E, H, I, d, bits, dead, seed=80, down_bits=down_bits)
+    x = synth.make_x(81, 5, 1, H, dt)
+    rng = np.random.default_rng(82)
+    ids = rng.choice(E, size=(1, k), replace=False).astype(np.int32)
+    if case == "repeated_id":
+        ids[0, 1] = ids[0, 0]
+    w = rng.random((1, k)).astype(np.float32)
+    y = _run_moe(gate, up, down, x, ids, w)
+    check_close(y, oracle.moe_ffn(gate, up, down, x, ids, w), case)
+
+
+def test_moe_decode_one_token_graph_replay():
+    """One-token FFN calls captured in a HIP graph: every replay, with eager
+    calls in between, gives the eager result bit for bit."""
+    E, k, H, I = 16, 8, 1024, 512
+    gate, up, down = _one_token_layer(E, H, I, seed=90)
+    G, U, D = _dev(gate), _dev(up), _dev(down)
+    wl = synth.MoEWorkload("one", E, k, H, I, 4, 9, 1, seed=91)
+    ws = torch.empty(vq.vq_moe_ffn_workspace_size(G, U, D, 1, k), dtype=torch.uint8, device="cuda")
+    steps = [synth.make_moe_inputs(wl, s) for s in range(3)]
+    xs = [x_to_torch(x) for x, _, _ in steps]
+    ids = [torch.from_numpy(i).cuda() for _, i, _ in steps]
+    ws_ = [torch.from_numpy(w).cuda() for _, _, w in steps]
+    outs = [torch.empty((1, H), dtype=torch.float32, device="cuda") for _ in steps]
+    eager = []
+    for s in range(3):
+        vq.vq_moe_ffn(G, U, D, xs[s], ids[s], ws_[s], out=outs[s], workspace=ws)
+        eager.append(outs[s].clone())
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in range(3):
+            vq.vq_moe_ffn(G, U, D, xs[s], ids[s], ws_[s], out=outs[s], workspace=ws)
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for s in range(3):
+            assert torch.equal(outs[s].view(torch.int32), eager[s].view(torch.int32)), (rep, s)
+        # eager work between replays
+        vq.vq_moe_ffn(G, U, D, xs[0], ids[0], ws_[0], workspace=ws)
+        torch.cuda.synchronize()

@@ -212,6 +212,34 @@ __device__ __forceinline__ float segment_sum_dpp(float v, int S)
     return v;
 }
 
+// n / d for a 64-bit n that nearly always fits 32 bits: the 32-bit
+// division is a short instruction sequence, the 64-bit one a long loop.
+__device__ __forceinline__ uint64_t udiv_small(uint64_t n, uint32_t d)
+{
+    if (n <= 0xffffffffull)
+        return (uint32_t)n / d;
+    return n / d;
+}
+
+// A load through the global address space (a pointer the compiler cannot
+// place would otherwise take a flat load, whose completion it tracks less
+// precisely).
+template <class T>
+__device__ __forceinline__ T load_global(const T *p)
+{
+    return *(const __attribute__((address_space(1))) T *)p;
+}
+
+// Largest value over aligned segments of 16 lanes (every lane gets it).
+__device__ __forceinline__ float segment_max16_dpp(float v)
+{
+    v = fmaxf(v, dpp_move<0xb1>(v));    // quad_perm [1,0,3,2]
+    v = fmaxf(v, dpp_move<0x4e>(v));    // quad_perm [2,3,0,1]
+    v = fmaxf(v, dpp_move<0x141>(v));   // row_half_mirror
+    v = fmaxf(v, dpp_move<0x140>(v));   // row_mirror
+    return v;
+}
+
 // Stage a tensor's codebook (K*d fp16 = K*d/2 dwords) into LDS.
 __device__ __forceinline__ void stage_codebook(uint32_t *__restrict__ lds,
                                                const uint16_t *__restrict__ cb, int n_dwords)

@@ -114,18 +114,20 @@ static int cu_count()
     return cached[dev];
 }
 
-hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream)
+// The engine's arguments and LDS layout for one launch: codebook 0 at dword
+// 0; codebook 1 at 2^bits*d/2 dwords when that offset is at most 32 KiB (the
+// kernel then uses it as a constant), else right after codebook 0; the work
+// lists last.  Returns the LDS dwords.
+static int rows_args(const RowsLaunch &L, RowsArgs &a, int &gpl)
 {
     const TensorDev &t0 = L.t[0];
-    const int gpl = (t0.groups + 63) / 64;
-    if (gpl > 2)
-        return hipErrorInvalidValue;
+    gpl = (t0.groups + 63) / 64;
     const int per_lane = (t0.groups + gpl - 1) / gpl;
     int s_log2 = 0;
     while ((1 << s_log2) < per_lane)
         ++s_log2;
     const int rpw = 64 >> s_log2;
-    RowsArgs a = {};
+    a = RowsArgs{};
     for (int p = 0; p < L.nproj; ++p) {
         a.codes[p] = L.t[p].codes;
         a.scales[p] = L.t[p].scales;
@@ -149,6 +151,24 @@ hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream)
     a.n_slots = L.n_slots;
     a.act_div = (L.ids && L.act_div > 0) ? L.act_div : 1;
     const int P = L.ids ? L.n_slots : L.n_act;
+    a.cb_offset[0] = 0;
+    const int cb1_fixed = (1 << t0.bits) * t0.d / 2;
+    a.cb_offset[1] = (cb1_fixed * 4 <= 32768) ? cb1_fixed : ((L.t[0].cb_dwords + 3) & ~3);
+    int off = L.nproj == 2 ? a.cb_offset[1] + L.t[1].cb_dwords : L.t[0].cb_dwords;
+    off = (off + 3) & ~3;
+    a.list_offset = off;
+    return off + list_dwords(P);
+}
+
+hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream)
+{
+    const TensorDev &t0 = L.t[0];
+    if (t0.groups > kMaxGroupsDecode)
+        return hipErrorInvalidValue;
+    RowsArgs a;
+    int gpl;
+    const size_t lds = (size_t)rows_args(L, a, gpl) * 4;
+    const int P = L.ids ? L.n_slots : L.n_act;
     if (P == 0 || t0.rows == 0)
         return hipSuccess;
     // a projection whose rows are all dead (skip-zero) stores nothing: every
@@ -157,18 +177,6 @@ hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream)
     for (int p = 0; p < L.nproj; ++p)
         if (L.t[p].n_stored == 0)
             return launch_fill_rows(L.out, P, t0.rows, L.out_stride, stream);
-
-    // LDS: codebook 0 at dword 0; codebook 1 at 2^bits*d/2 dwords when that
-    // offset is at most 32 KiB (the kernel then uses it as a constant), else
-    // right after codebook 0; the work lists last
-    a.cb_offset[0] = 0;
-    const int cb1_fixed = (1 << t0.bits) * t0.d / 2;
-    a.cb_offset[1] = (cb1_fixed * 4 <= 32768) ? cb1_fixed : ((L.t[0].cb_dwords + 3) & ~3);
-    int off = L.nproj == 2 ? a.cb_offset[1] + L.t[1].cb_dwords : L.t[0].cb_dwords;
-    off = (off + 3) & ~3;
-    a.list_offset = off;
-    off += list_dwords(P);
-    const size_t lds = (size_t)off * 4;
 
     const int64_t units = (int64_t)P * a.tiles;
     const int n_cu = cu_count();
@@ -180,44 +188,10 @@ hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream)
     }
 }
 
-// LDS of the fused down projection and combine (0: not applicable).
-static size_t mix_lds_bytes(const TensorDev &dn, int n_tok, int top_k, int &list_off, int &x_off,
-                            int &m_off, int &y_off)
+// The fused down projection and combine: everything but the LDS layout.
+static void mix_args(const TensorDev &dn, int n_tok, int top_k, const float *h, const int32_t *ids,
+                     const float *w, float *y, MixArgs &a)
 {
-    const int P = n_tok * top_k;
-    if (dn.groups > 64 || n_tok > 16 || P > kMaxSlots)
-        return 0;
-    int off = (dn.cb_dwords + 3) & ~3;
-    list_off = off;
-    off += (list_dwords(P) + 3) & ~3;
-    x_off = off;
-    off += P * dn.groups * kMixXStride;
-    m_off = off;
-    off += (P * dn.groups + 3) & ~3;
-    y_off = off;
-    off += kWaves * 64 * n_tok;
-    const size_t bytes = (size_t)off * 4;
-    return bytes <= 65536 ? bytes : 0;
-}
-
-bool mix_supported(const TensorDev &dn, int n_tok, int top_k)
-{
-    int l, x, m, y;
-    return mix_lds_bytes(dn, n_tok, top_k, l, x, m, y) != 0;
-}
-
-hipError_t launch_mix(const TensorDev &dn, int n_tok, int top_k, const float *h,
-                      const int32_t *ids, const float *w, float *y, hipStream_t stream)
-{
-    if (n_tok == 0 || dn.rows == 0)
-        return hipSuccess;
-    if (dn.n_stored == 0)
-        return launch_fill_rows(y, n_tok, dn.rows, dn.rows, stream);
-    MixArgs a = {};
-    const size_t lds = mix_lds_bytes(dn, n_tok, top_k, a.list_offset, a.x_offset, a.m_offset,
-                                     a.y_offset);
-    if (lds == 0)
-        return hipErrorInvalidValue;
     int s_log2 = 0;
     while ((1 << s_log2) < dn.groups)
         ++s_log2;
@@ -239,6 +213,47 @@ hipError_t launch_mix(const TensorDev &dn, int n_tok, int top_k, const float *h,
     const int rpw = 64 >> s_log2;
     a.units = (dn.rows + rpw - 1) / rpw;
     a.max_wgs = 2 * cu_count();
+}
+
+// Its LDS from dword list_off on (the codebook sits below, from dword 0):
+// routing lists, staged h, h's factors, the waves' partial sums.  Returns the
+// end in dwords (0: not applicable).
+static int mix_layout(const TensorDev &dn, int n_tok, int top_k, int list_off, MixArgs &a)
+{
+    const int P = n_tok * top_k;
+    if (dn.groups > 64 || n_tok > 16 || P > kMaxSlots)
+        return 0;
+    int off = list_off;
+    a.list_offset = off;
+    off += (list_dwords(P) + 3) & ~3;
+    a.x_offset = off;
+    off += P * dn.groups * kMixXStride;
+    a.m_offset = off;
+    off += (P * dn.groups + 3) & ~3;
+    a.y_offset = off;
+    off += kWaves * 64 * n_tok;
+    return (size_t)off * 4 <= 65536 ? off : 0;
+}
+
+bool mix_supported(const TensorDev &dn, int n_tok, int top_k)
+{
+    MixArgs a = {};
+    return mix_layout(dn, n_tok, top_k, (dn.cb_dwords + 3) & ~3, a) != 0;
+}
+
+hipError_t launch_mix(const TensorDev &dn, int n_tok, int top_k, const float *h,
+                      const int32_t *ids, const float *w, float *y, hipStream_t stream)
+{
+    if (n_tok == 0 || dn.rows == 0)
+        return hipSuccess;
+    if (dn.n_stored == 0)
+        return launch_fill_rows(y, n_tok, dn.rows, dn.rows, stream);
+    MixArgs a = {};
+    const int end = mix_layout(dn, n_tok, top_k, (dn.cb_dwords + 3) & ~3, a);
+    if (end == 0)
+        return hipErrorInvalidValue;
+    mix_args(dn, n_tok, top_k, h, ids, w, y, a);
+    const size_t lds = (size_t)end * 4;
     switch (dn.d) {
     case 2: return mix_d<2>(dn.bits, a, lds, stream);
     case 4: return mix_d<4>(dn.bits, a, lds, stream);

@@ -225,9 +225,12 @@ struct RowRegs {
 // unconditional; rows past the end and dead rows read stored row 0 and are
 // zeroed afterwards -- the host never launches for a tensor with no stored
 // rows).  The stored-row lookup (row map) is one dependent load.
-template <int D, int BITS, int GPL, int NPROJ, int ITERS>
-__device__ __forceinline__ void load_rows(const RowsArgs &a, int e, int row0, int rpw, int seg,
-                                          int sl, int S, RowRegs<D, BITS, GPL, NPROJ> (&rr)[ITERS])
+// MAP: some projection has a row map.  Without one no load depends on
+// another, so nothing waits for loads issued earlier.
+template <int D, int BITS, int GPL, int NPROJ, int ITERS, bool MAP>
+__device__ __forceinline__ void load_rows_m(const RowsArgs &a, int e, int row0, int rpw, int seg,
+                                            int sl, int S,
+                                            RowRegs<D, BITS, GPL, NPROJ> (&rr)[ITERS])
 {
     using GM = Geom<D, BITS>;
     constexpr int NW = GM::NW;
@@ -238,7 +241,7 @@ __device__ __forceinline__ void load_rows(const RowsArgs &a, int e, int row0, in
         const int64_t lin = (int64_t)e * a.rows + min(r, a.rows - 1);
 #pragma unroll
         for (int p = 0; p < NPROJ; ++p)
-            srow[it][p] = a.row_map[p] ? a.row_map[p][lin] : (int)lin;
+            srow[it][p] = (MAP && a.row_map[p]) ? a.row_map[p][lin] : (int)lin;
     }
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
@@ -267,6 +270,20 @@ __device__ __forceinline__ void load_rows(const RowsArgs &a, int e, int row0, in
             }
         }
     }
+}
+
+template <int D, int BITS, int GPL, int NPROJ, int ITERS>
+__device__ __forceinline__ void load_rows(const RowsArgs &a, int e, int row0, int rpw, int seg,
+                                          int sl, int S, RowRegs<D, BITS, GPL, NPROJ> (&rr)[ITERS])
+{
+    bool map = false;
+#pragma unroll
+    for (int p = 0; p < NPROJ; ++p)
+        map = map || a.row_map[p] != nullptr;
+    if (map)
+        load_rows_m<D, BITS, GPL, NPROJ, ITERS, true>(a, e, row0, rpw, seg, sl, S, rr);
+    else
+        load_rows_m<D, BITS, GPL, NPROJ, ITERS, false>(a, e, row0, rpw, seg, sl, S, rr);
 }
 
 template <int D, int BITS, int GPL, int NPROJ, bool HL, int ITERS>
@@ -345,46 +362,57 @@ struct CbRegs {
     uint4 v[NPROJ][cb_batch<D, BITS>()];
 };
 
+// The first B*kThreads uint4 of a codebook, one slot per thread and batch.
+template <int B>
+__device__ __forceinline__ void cb_to_regs(const uint16_t *cb, int dwords, uint4 (&v)[B])
+{
+    const uint4 *src = reinterpret_cast<const uint4 *>(cb);
+    const int n4 = dwords >> 2;
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+        const int i = threadIdx.x + j * kThreads;
+        v[j] = (i < n4) ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// The codebook into LDS at base: the register batches, then the rest
+// (codebooks beyond B*16*kThreads bytes, and a tail of fewer than four
+// dwords) straight from global memory.
+template <int B>
+__device__ __forceinline__ void cb_regs_to_lds(const uint16_t *cb, int dwords, const uint4 (&v)[B],
+                                               uint32_t *__restrict__ base)
+{
+    uint4 *dst = reinterpret_cast<uint4 *>(base);
+    const int n4 = dwords >> 2;
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+        const int i = threadIdx.x + j * kThreads;
+        if (i < n4)
+            dst[i] = v[j];
+    }
+    const uint32_t *s32 = reinterpret_cast<const uint32_t *>(cb);
+    for (int i = 4 * B * kThreads + threadIdx.x * 4; i + 3 < dwords; i += 4 * kThreads)
+        *reinterpret_cast<uint4 *>(base + i) = *reinterpret_cast<const uint4 *>(s32 + i);
+    for (int i = (n4 << 2) + threadIdx.x; i < dwords; i += kThreads)
+        base[i] = s32[i];
+}
+
 template <int D, int BITS, int NPROJ>
 __device__ __forceinline__ void load_codebooks(const RowsArgs &a, CbRegs<D, BITS, NPROJ> &cr)
 {
-    constexpr int B = cb_batch<D, BITS>();
 #pragma unroll
-    for (int p = 0; p < NPROJ; ++p) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(a.codebook[p]);
-        const int n4 = a.cb_dwords[p] >> 2;
-#pragma unroll
-        for (int j = 0; j < B; ++j) {
-            const int i = threadIdx.x + j * kThreads;
-            cr.v[p][j] = (i < n4) ? src[i] : make_uint4(0u, 0u, 0u, 0u);
-        }
-    }
+    for (int p = 0; p < NPROJ; ++p)
+        cb_to_regs(a.codebook[p], a.cb_dwords[p], cr.v[p]);
 }
 
 template <int D, int BITS, int NPROJ>
 __device__ __forceinline__ void store_codebooks(const RowsArgs &a, const CbRegs<D, BITS, NPROJ> &cr,
                                                 uint32_t *__restrict__ lds)
 {
-    constexpr int B = cb_batch<D, BITS>();
 #pragma unroll
-    for (int p = 0; p < NPROJ; ++p) {
-        uint32_t *base = lds + (p == 0 ? 0 : cb1_offset<D, BITS>(a));
-        uint4 *dst = reinterpret_cast<uint4 *>(base);
-        const int n4 = a.cb_dwords[p] >> 2;
-#pragma unroll
-        for (int j = 0; j < B; ++j) {
-            const int i = threadIdx.x + j * kThreads;
-            if (i < n4)
-                dst[i] = cr.v[p][j];
-        }
-        // the rest: codebooks beyond B*16*kThreads bytes, and a tail of fewer
-        // than four dwords
-        const uint32_t *s32 = reinterpret_cast<const uint32_t *>(a.codebook[p]);
-        for (int i = 4 * B * kThreads + threadIdx.x * 4; i + 3 < a.cb_dwords[p]; i += 4 * kThreads)
-            *reinterpret_cast<uint4 *>(base + i) = *reinterpret_cast<const uint4 *>(s32 + i);
-        for (int i = (n4 << 2) + threadIdx.x; i < a.cb_dwords[p]; i += kThreads)
-            base[i] = s32[i];
-    }
+    for (int p = 0; p < NPROJ; ++p)
+        cb_regs_to_lds(a.codebook[p], a.cb_dwords[p], cr.v[p],
+                       lds + (p == 0 ? 0 : cb1_offset<D, BITS>(a)));
 }
 
 // Work lists in LDS, from list_offset (P = number of pairs):
@@ -516,8 +544,8 @@ __global__ __launch_bounds__(kThreads) void k_rows(const RowsArgs a)
     const int seg = lane >> a.S_log2;
     const int sl = lane & (S - 1);
     const int64_t n_units = (int64_t)P * a.tiles;
-    int64_t k = (int64_t)blockIdx.x * n_units / gridDim.x;
-    const int64_t k_end = (int64_t)(blockIdx.x + 1) * n_units / gridDim.x;
+    int64_t k = (int64_t)udiv_small((uint64_t)blockIdx.x * n_units, gridDim.x);
+    const int64_t k_end = (int64_t)udiv_small((uint64_t)(blockIdx.x + 1) * n_units, gridDim.x);
     struct Unit {
         int item, e, row0;
     };
@@ -529,11 +557,11 @@ __global__ __launch_bounds__(kThreads) void k_rows(const RowsArgs a)
     const bool direct = one_token || !a.ids;
     if (direct && k < k_end) {
         if (one_token) {
-            ua.item = (int)(k / a.tiles);
-            ua.e = a.ids[ua.item];
+            ua.item = (int)udiv_small(k, a.tiles);
+            ua.e = load_global(a.ids + ua.item);
             ua.row0 = (int)(k - (int64_t)ua.item * a.tiles) * a.tile_rows + wave * ITERS * rpw;
         } else {
-            const int t = (int)(k / P);
+            const int t = (int)udiv_small(k, P);
             ua.item = (int)(k - (int64_t)t * P);
             ua.e = a.expert;
             ua.row0 = t * a.tile_rows + wave * ITERS * rpw;
@@ -576,7 +604,7 @@ __global__ __launch_bounds__(kThreads) void k_rows(const RowsArgs a)
         const int u0 = L.ustart[u];
         const int nu = L.ustart[u + 1] - u0;
         const int64_t rel = kk - (int64_t)u0 * a.tiles;
-        const int t = (int)(rel / nu);
+        const int t = (int)udiv_small(rel, nu);
         Unit un;
         un.item = L.items[u0 + (int)(rel - (int64_t)t * nu)];
         un.e = L.uexp[u];
@@ -622,6 +650,7 @@ __global__ __launch_bounds__(kThreads) void k_rows(const RowsArgs a)
         ++k;
     }
 }
+
 
 // --------------------------------------------------------------------------------
 // exact dequantize: one thread per (row, group)
@@ -733,62 +762,109 @@ struct MixArgs {
 constexpr int kMixXStride = 36;   // dwords per (pair, group): 32 used, padded for ds_read_b128
 constexpr int kMixChunk = 4;      // experts whose rows are loaded together
 
+// The engine of k_mix, in the pieces a caller runs in order: load_item(first)
+// (optional, before the setup), the setup (stage_codebook, stage_lists,
+// stage_h, finish_setup), then run().
+//
+// A workgroup walks tiles of rpw output rows (blockIdx.x, + gridDim.x,
+// ...); its waves split the distinct experts into contiguous ranges of at
+// most per = ceil(U / waves), taken kMixChunk at a time.  Work item i of a
+// wave is (tile i / nch, chunk i % nch); the words of item i+1 are in flight
+// while item i is computed.  For a single token the experts are the ids
+// themselves, so the first item can be requested before the setup and its
+// memory latency overlaps it.
 template <int D, int BITS>
-__global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
-{
+struct MixEngine {
     using GM = Geom<D, BITS>;
-    constexpr int NW = GM::NW;
-    constexpr int G = GM::G;
-    constexpr int HP = D / 2;
-    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int P = a.n_tok * a.top_k;
-
-    const int S = 1 << a.S_log2;
-    const int rpw = 64 >> a.S_log2;
-    const int seg = lane >> a.S_log2;
-    const int sl = lane & (S - 1);
-    const int g = min(sl, a.groups - 1);
-    const bool gok = sl < a.groups;
-    const bool one = a.n_tok == 1;
-    const Lists L = lists_at(lds, a.list_offset, P);
-
-    // A workgroup walks tiles of rpw output rows (blockIdx.x, + gridDim.x,
-    // ...); its waves split the distinct experts into contiguous ranges of
-    // at most per = ceil(U / waves), taken kMixChunk at a time.  Work item i
-    // of a wave is (tile i / nch, chunk i % nch); the words of item i+1 are
-    // in flight while item i is computed.  For a single token the experts
-    // are the ids themselves, so the first item is requested before the
-    // setup below and its memory latency overlaps it.
+    static constexpr int NW = GM::NW;
+    static constexpr int G = GM::G;
+    static constexpr int HP = D / 2;
     struct Chunk {
         uint32_t wd[kMixChunk][NW];
         uint32_t sc[kMixChunk];
         int live;
     };
-    auto wave_range = [&](int U, int &ub, int &ue, int &nch) {
+
+    const MixArgs &a;
+    uint32_t *lds;
+    int tid, lane, wave, P, S, rpw, seg, sl, g;
+    bool gok, one;
+    Lists L;
+    int my_units;
+    int ub = 0, ue = 0, nch = 1;
+
+    __device__ __forceinline__ MixEngine(const MixArgs &args, uint32_t *l) : a(args), lds(l)
+    {
+        tid = threadIdx.x;
+        lane = tid & 63;
+        wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: expert ids load as scalars
+        P = a.n_tok * a.top_k;
+        S = 1 << a.S_log2;
+        rpw = 64 >> a.S_log2;
+        seg = lane >> a.S_log2;
+        sl = lane & (S - 1);
+        g = min(sl, a.groups - 1);
+        gok = sl < a.groups;
+        one = a.n_tok == 1;
+        L = lists_at(lds, a.list_offset, P);
+        my_units = (int)blockIdx.x < a.units
+                       ? (a.units - 1 - (int)blockIdx.x) / (int)gridDim.x + 1
+                       : 0;
+        if (one)
+            wave_range(P);
+    }
+
+    __device__ __forceinline__ void wave_range(int U)
+    {
         const int per = (U + kWaves - 1) / kWaves;
         ub = min(wave * per, U);
         ue = min(ub + per, U);
         nch = max(1, (per + kMixChunk - 1) / kMixChunk);   // the same for every wave
-    };
-    const int my_units =
-        (int)blockIdx.x < a.units ? (a.units - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
-    // every load unconditional (entries past the range repeat its last
-    // expert and are skipped)
-    auto load_item = [&](Chunk &ck, int item, int ub, int ue, int nch) {
-        const int unit = blockIdx.x + (item / nch) * gridDim.x;
+    }
+
+    __device__ __forceinline__ int n_items() const { return my_units * nch; }
+
+    // The experts of an item's chunk (entries past the wave's range repeat
+    // its last expert and are skipped).
+    __device__ __forceinline__ void experts_of(int item, int (&e)[kMixChunk]) const
+    {
         const int u0 = ub + (item % nch) * kMixChunk;
+#pragma unroll
+        for (int c = 0; c < kMixChunk; ++c) {
+            const int u = max(min(u0 + c, ue - 1), 0);
+            e[c] = one ? load_global(a.ids + u) : L.uexp[u];
+        }
+    }
+
+    __device__ __forceinline__ void load_item(Chunk &ck, int item) const
+    {
+        int e[kMixChunk];
+        experts_of(item, e);
+        load_item(ck, item, e);
+    }
+
+    __device__ __forceinline__ void load_item(Chunk &ck, int item, const int (&e)[kMixChunk]) const
+    {
+        if (a.row_map)
+            load_item_m<true>(ck, item, e);
+        else
+            load_item_m<false>(ck, item, e);
+    }
+
+    // every load unconditional; MAP: the stored rows come from the row map
+    // (without one no load waits for loads issued earlier)
+    template <bool MAP>
+    __device__ __forceinline__ void load_item_m(Chunk &ck, int item,
+                                                const int (&e)[kMixChunk]) const
+    {
+        const int unit = blockIdx.x + (item / nch) * gridDim.x;
         const int r = unit * rpw + seg;
         const bool rok = r < a.rows;
         int64_t srow[kMixChunk];
 #pragma unroll
         for (int c = 0; c < kMixChunk; ++c) {
-            const int u = max(min(u0 + c, ue - 1), 0);
-            const int e = one ? a.ids[u] : L.uexp[u];
-            const int64_t lin = (int64_t)e * a.rows + min(r, a.rows - 1);
-            srow[c] = a.row_map ? a.row_map[lin] : lin;
+            const int64_t lin = (int64_t)e[c] * a.rows + min(r, a.rows - 1);
+            srow[c] = MAP ? a.row_map[lin] : lin;
         }
         ck.live = 0;
 #pragma unroll
@@ -807,19 +883,10 @@ __global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
             }
             ck.sc[c] = a.scales[sr * a.groups + g];
         }
-    };
-    Chunk ca, cb;
-    int ub, ue, nch;
-    bool preloaded = false;
-    if (one) {
-        wave_range(P, ub, ue, nch);
-        if (my_units > 0) {
-            load_item(ca, 0, ub, ue, nch);
-            preloaded = true;
-        }
     }
 
     // ---- setup: codebook, routing lists, h as range-scaled fp16 pairs ------------
+    __device__ __forceinline__ void stage_codebook() const
     {
         const uint4 *src = reinterpret_cast<const uint4 *>(a.codebook);
         const int n4 = a.cb_dwords >> 2;
@@ -829,53 +896,75 @@ __global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
         for (int i = (n4 << 2) + tid; i < a.cb_dwords; i += kThreads)
             lds[i] = s32[i];
     }
-    if (one)
-        single_token_lists(L, a.ids, P);
-    else
-        for (int q = tid; q < P; q += kThreads)
-            L.ids[q] = a.ids[q];
-    uint32_t *xs = lds + a.x_offset;                    // [P][groups][kMixXStride]
-    float *xm = reinterpret_cast<float *>(lds + a.m_offset);   // [P][groups]
-    for (int it = tid; it < P * a.groups; it += kThreads) {
-        const int q = it / a.groups;
-        const int gg = it - q * a.groups;
-        const float4 *src = reinterpret_cast<const float4 *>(a.h + ((int64_t)q * a.groups + gg) * 64);
-        float4 v[16];
-        float amax = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            v[j] = src[j];
-            amax = fmaxf(fmaxf(amax, fmaxf(fabsf(v[j].x), fabsf(v[j].y))),
-                         fmaxf(fabsf(v[j].z), fabsf(v[j].w)));
-        }
-        const int k = range_exponent(amax);
-        const float up = ldexpf(1.0f, k);
-        uint4 *dst = reinterpret_cast<uint4 *>(xs + (size_t)it * kMixXStride);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            union { f16x2 h[4]; uint4 u; } o;
-            o.h[0] = pack_f16x2(v[2 * j].x * up, v[2 * j].y * up);
-            o.h[1] = pack_f16x2(v[2 * j].z * up, v[2 * j].w * up);
-            o.h[2] = pack_f16x2(v[2 * j + 1].x * up, v[2 * j + 1].y * up);
-            o.h[3] = pack_f16x2(v[2 * j + 1].z * up, v[2 * j + 1].w * up);
-            dst[j] = o.u;
-        }
-        xm[it] = ldexpf(1.0f, -k);
+
+    __device__ __forceinline__ void stage_lists() const
+    {
+        if (one)
+            single_token_lists(L, a.ids, P);
+        else
+            for (int q = tid; q < P; q += kThreads)
+                L.ids[q] = a.ids[q];
     }
-    __syncthreads();
-    if (!one)
-        build_lists(L, P);
-    const int U = *L.U;
-    if (!one)
-        wave_range(U, ub, ue, nch);
+
+    // h as range-scaled fp16 pairs.  The 64 floats of a (pair, group) are
+    // read by 16 consecutive lanes, 16 bytes each, their largest magnitude
+    // found across those lanes, and each lane writes its four values as two
+    // fp16 pairs.  Up to kHPasses passes of 16 (pair, group)s per workgroup
+    // have their loads in flight together.
+    __device__ __forceinline__ void stage_h() const
+    {
+        constexpr int kPerPass = kThreads / 16;
+        constexpr int kHPasses = 8;
+        uint32_t *xs = lds + a.x_offset;                           // [P][groups][kMixXStride]
+        float *xm = reinterpret_cast<float *>(lds + a.m_offset);   // [P][groups]
+        const int n = P * a.groups;    // (pair, group) items; item i is h[64 i, 64 i + 64)
+        const int piece = tid & 15;
+        for (int base = 0; base < n; base += kPerPass * kHPasses) {
+            float4 v[kHPasses];
+#pragma unroll
+            for (int j = 0; j < kHPasses; ++j) {
+                const int it = min(base + j * kPerPass + (tid >> 4), n - 1);
+                const float4 *src = reinterpret_cast<const float4 *>(a.h) + (size_t)it * 16 + piece;
+                v[j] = *src;
+            }
+#pragma unroll
+            for (int j = 0; j < kHPasses; ++j) {
+                const int it = base + j * kPerPass + (tid >> 4);
+                const float m4 = fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)),
+                                       fmaxf(fabsf(v[j].z), fabsf(v[j].w)));
+                const int k = range_exponent(segment_max16_dpp(m4));
+                const float up = ldexpf(1.0f, k);
+                union { f16x2 h[2]; uint2 u; } o;
+                o.h[0] = pack_f16x2(v[j].x * up, v[j].y * up);
+                o.h[1] = pack_f16x2(v[j].z * up, v[j].w * up);
+                if (it < n) {
+                    *reinterpret_cast<uint2 *>(xs + (size_t)it * kMixXStride + 2 * piece) = o.u;
+                    if (piece == 0)
+                        xm[it] = ldexpf(1.0f, -k);
+                }
+            }
+        }
+    }
+
+    // After the stage_* calls: lists for several tokens and the waves' ranges.
+    __device__ __forceinline__ void finish_setup()
+    {
+        __syncthreads();
+        if (!one) {
+            build_lists(L, P);
+            wave_range(*L.U);
+        }
+    }
 
     // ---- the work items ----------------------------------------------------------------
     // yacc[w][row][t]: wave w's partial sums of the current tile, added in
     // wave order when the tile is done
-    float *yall = reinterpret_cast<float *>(lds + a.y_offset);
-    float *yacc = yall + wave * 64 * a.n_tok;
-    const int n_items = my_units * nch;
-    auto process = [&](const Chunk &ck, int item) {
+    __device__ __forceinline__ void process(const Chunk &ck, int item) const
+    {
+        const uint32_t *xs = lds + a.x_offset;
+        const float *xm = reinterpret_cast<const float *>(lds + a.m_offset);
+        float *yall = reinterpret_cast<float *>(lds + a.y_offset);
+        float *yacc = yall + wave * 64 * a.n_tok;
         const int tile = item / nch;
         const int ch = item - tile * nch;
         const int unit = blockIdx.x + tile * gridDim.x;
@@ -929,21 +1018,43 @@ __global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
             }
             __syncthreads();
         }
-    };
-    if (n_items == 0)
-        return;
-    if (!preloaded)
-        load_item(ca, 0, ub, ue, nch);
-    for (int i = 0; i < n_items; i += 2) {
-        if (i + 1 < n_items)
-            load_item(cb, i + 1, ub, ue, nch);
-        process(ca, i);
-        if (i + 1 >= n_items)
-            break;
-        if (i + 2 < n_items)
-            load_item(ca, i + 2, ub, ue, nch);
-        process(cb, i + 1);
     }
+
+    // ca holds item 0 if preloaded; items alternate between ca and cb
+    __device__ __forceinline__ void run(Chunk &ca, Chunk &cb, bool preloaded) const
+    {
+        const int n = n_items();
+        if (n == 0)
+            return;
+        if (!preloaded)
+            load_item(ca, 0);
+        for (int i = 0; i < n; i += 2) {
+            if (i + 1 < n)
+                load_item(cb, i + 1);
+            process(ca, i);
+            if (i + 1 >= n)
+                break;
+            if (i + 2 < n)
+                load_item(ca, i + 2);
+            process(cb, i + 1);
+        }
+    }
+};
+
+template <int D, int BITS>
+__global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
+    MixEngine<D, BITS> m(a, lds);
+    typename MixEngine<D, BITS>::Chunk ca, cb;
+    const bool pre = m.one && m.my_units > 0;
+    if (pre)
+        m.load_item(ca, 0);
+    m.stage_codebook();
+    m.stage_lists();
+    m.stage_h();
+    m.finish_setup();
+    m.run(ca, cb, pre);
 }
 
 template <int D, int BITS>

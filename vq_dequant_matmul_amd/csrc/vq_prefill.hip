@@ -22,6 +22,7 @@ VQ_DECL_GEMM(8)
 #undef VQ_DECL_GEMM
 
 constexpr int kRouteThreads = 1024;
+constexpr int kRouteBatch = 8;   // ids per thread loaded together
 constexpr int kMaxRouteExperts = 4096;
 
 // Exclusive scan of v[0..n) in place (n <= 4 * kRouteThreads); returns the
@@ -112,8 +113,20 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const int32_t *__restri
         fill[e] = 0;
     }
     __syncthreads();
-    for (int q = tid; q < P; q += kRouteThreads)
-        atomicAdd(&cnt[ids[q]], 1);
+    // the ids are read kRouteBatch per thread at a time, so their loads are
+    // in flight together instead of one round trip per id
+    for (int q0 = 0; q0 < P; q0 += kRouteThreads * kRouteBatch) {
+        int id[kRouteBatch];
+#pragma unroll
+        for (int k = 0; k < kRouteBatch; ++k) {
+            const int q = q0 + k * kRouteThreads + tid;
+            id[k] = q < P ? ids[q] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kRouteBatch; ++k)
+            if (q0 + k * kRouteThreads + tid < P)
+                atomicAdd(&cnt[id[k]], 1);
+    }
     __syncthreads();
     for (int e = tid; e < E; e += kRouteThreads)
         base[e] = cnt[e];
@@ -123,11 +136,22 @@ __global__ __launch_bounds__(kRouteThreads) void k_route(const int32_t *__restri
         offs[e] = base[e];
     if (tid == 0)
         offs[E] = total;
-    for (int q = tid; q < P; q += kRouteThreads) {
-        const int e = ids[q];
-        const int p = base[e] + atomicAdd(&fill[e], 1);
-        perm[p] = q;
-        pos[q] = p;
+    for (int q0 = 0; q0 < P; q0 += kRouteThreads * kRouteBatch) {
+        int id[kRouteBatch];
+#pragma unroll
+        for (int k = 0; k < kRouteBatch; ++k) {
+            const int q = q0 + k * kRouteThreads + tid;
+            id[k] = q < P ? ids[q] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kRouteBatch; ++k) {
+            const int q = q0 + k * kRouteThreads + tid;
+            if (q < P) {
+                const int p = base[id[k]] + atomicAdd(&fill[id[k]], 1);
+                perm[p] = q;
+                pos[q] = p;
+            }
+        }
     }
     __syncthreads();
     build_tiles(cnt, base, toff, E, mt, tiles, n_tiles, scratch);
@@ -152,6 +176,11 @@ __global__ __launch_bounds__(kRouteThreads) void k_tiles_from_offsets(
 // [2^14, 2^15) and converted to fp16 (exact for bf16 input in fp16's normal
 // range, rounded to nearest for fp32); k[row] receives the exponent.  One
 // wave per row.
+// Rows of up to kRowRegs 16-byte chunks per lane are read once (the chunks
+// stay in registers between the max and the conversion); longer rows read
+// the rest again.
+constexpr int kRowRegs = 8;
+
 __global__ __launch_bounds__(256) void k_rowscale(const void *__restrict__ x, int f32, int rows,
                                                   int cols, int64_t stride, f16 *__restrict__ out,
                                                   int32_t *__restrict__ k)
@@ -161,46 +190,48 @@ __global__ __launch_bounds__(256) void k_rowscale(const void *__restrict__ x, in
     if (row >= rows)
         return;
     f16 *o = out + (int64_t)row * cols;
+    // elements per 16-byte chunk and per pass of the wave
+    const int per = f32 ? 4 : 8;
+    const int step = 64 * per;
+    const char *p = static_cast<const char *>(x) + (int64_t)row * stride * (f32 ? 4 : 2);
+    const int esz = f32 ? 4 : 2;
+    auto absmax = [&](const uint4 &q) -> uint32_t {
+        if (f32)
+            return max(max(q.x & 0x7fffffffu, q.y & 0x7fffffffu),
+                       max(q.z & 0x7fffffffu, q.w & 0x7fffffffu));
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            m = max(m, max((w[j] & 0x7fffu) << 16, (w[j] >> 16 & 0x7fffu) << 16));
+        return m;
+    };
+    uint4 cache[kRowRegs];
     uint32_t mx = 0;
-    if (f32) {
-        const float *p = static_cast<const float *>(x) + (int64_t)row * stride;
-        for (int c = lane * 4; c < cols; c += 256) {
-            const uint4 q = *reinterpret_cast<const uint4 *>(p + c);
-            mx = max(mx, max(max(q.x & 0x7fffffffu, q.y & 0x7fffffffu),
-                             max(q.z & 0x7fffffffu, q.w & 0x7fffffffu)));
-        }
 #pragma unroll
-        for (int o2 = 32; o2 >= 1; o2 >>= 1)
-            mx = max(mx, (uint32_t)__shfl_xor((int)mx, o2, 64));
-        const int ex = range_exponent(__uint_as_float(mx));
-        const float up = ldexpf(1.0f, ex);
-        for (int c = lane * 4; c < cols; c += 256) {
-            const float4 q = *reinterpret_cast<const float4 *>(p + c);
+    for (int i = 0; i < kRowRegs; ++i) {
+        const int c = lane * per + i * step;
+        if (c < cols) {
+            cache[i] = *reinterpret_cast<const uint4 *>(p + (int64_t)c * esz);
+            mx = max(mx, absmax(cache[i]));
+        }
+    }
+    for (int c = lane * per + kRowRegs * step; c < cols; c += step)
+        mx = max(mx, absmax(*reinterpret_cast<const uint4 *>(p + (int64_t)c * esz)));
+#pragma unroll
+    for (int o2 = 32; o2 >= 1; o2 >>= 1)
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o2, 64));
+    const int ex = range_exponent(__uint_as_float(mx));
+    const float up = ldexpf(1.0f, ex);
+    auto convert = [&](const uint4 &q, int c) {
+        if (f32) {
             union { f16x4 v; uint2 u; } h;
-            h.v[0] = (f16)(q.x * up);
-            h.v[1] = (f16)(q.y * up);
-            h.v[2] = (f16)(q.z * up);
-            h.v[3] = (f16)(q.w * up);
+            h.v[0] = (f16)(__uint_as_float(q.x) * up);
+            h.v[1] = (f16)(__uint_as_float(q.y) * up);
+            h.v[2] = (f16)(__uint_as_float(q.z) * up);
+            h.v[3] = (f16)(__uint_as_float(q.w) * up);
             *reinterpret_cast<uint2 *>(o + c) = h.u;
-        }
-        if (lane == 0)
-            k[row] = ex;
-    } else {
-        const uint16_t *p = static_cast<const uint16_t *>(x) + (int64_t)row * stride;
-        for (int c = lane * 8; c < cols; c += 512) {
-            const uint4 q = *reinterpret_cast<const uint4 *>(p + c);
-            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                mx = max(mx, max((w[j] & 0x7fffu) << 16, (w[j] >> 16 & 0x7fffu) << 16));
-        }
-#pragma unroll
-        for (int o2 = 32; o2 >= 1; o2 >>= 1)
-            mx = max(mx, (uint32_t)__shfl_xor((int)mx, o2, 64));
-        const int ex = range_exponent(__uint_as_float(mx));
-        const float up = ldexpf(1.0f, ex);
-        for (int c = lane * 8; c < cols; c += 512) {
-            const uint4 q = *reinterpret_cast<const uint4 *>(p + c);
+        } else {
             const uint32_t w[4] = {q.x, q.y, q.z, q.w};
             union { f16x8 v; uint4 u; } h;
 #pragma unroll
@@ -210,9 +241,17 @@ __global__ __launch_bounds__(256) void k_rowscale(const void *__restrict__ x, in
             }
             *reinterpret_cast<uint4 *>(o + c) = h.u;
         }
-        if (lane == 0)
-            k[row] = ex;
+    };
+#pragma unroll
+    for (int i = 0; i < kRowRegs; ++i) {
+        const int c = lane * per + i * step;
+        if (c < cols)
+            convert(cache[i], c);
     }
+    for (int c = lane * per + kRowRegs * step; c < cols; c += step)
+        convert(*reinterpret_cast<const uint4 *>(p + (int64_t)c * esz), c);
+    if (lane == 0)
+        k[row] = ex;
 }
 
 // y[t][c] = sum over slots s (in order) of w[t][s] * z[pos[t*k + s]][c].

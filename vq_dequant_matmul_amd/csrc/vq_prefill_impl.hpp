@@ -497,11 +497,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
                     for (int pb = 0; pb < NPB; ++pb)
                         scale(bf[pb][j - 1], s2[pb]);
                 }
-                // interleave the side work with the MFMAs of this slice
+                // interleave the side work with the MFMAs of this slice (a
+                // sweep of the pattern on full-size layers put two LDS reads
+                // and four VALU per MFMA a few percent ahead of one and three)
                 static_for<NB * NPB>([&](auto) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);   // three VALU
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
                 });
                 __builtin_amdgcn_sched_barrier(0);
             });

@@ -11,7 +11,8 @@ Card", changelog 2026-10-01 "vq-skipzero"; "GLM-5.3-Flash-VQ-2.7bpw",
 section "Methodology"): unpack b-bit codes from row-local uint32 streams,
 decode W = scale * codebook[code] exactly in fp32, multiply with fp64
 accumulation, and for the MoE FFN apply SwiGLU and the gate-weighted sum over
-the routed experts in fp64.
+the routed experts in fp64.  ``gather`` reads single decoded rows, as the
+per-layer n-gram embedding tables of "Qwen3.8-Flash-Next-VQ-4.4bpw" are read.
 
 Tensor arguments are any object with the attributes ``rows, cols, d, bits, K,
 n_experts, codebook (uint16 [K, d]), codes (uint32 [n_stored, wpr]), scales
@@ -79,6 +80,8 @@ def _load():
         lib.vqo_check.argtypes = [P]
         lib.vqo_decode.restype = ctypes.c_int
         lib.vqo_decode.argtypes = [P, ctypes.c_int32, P]
+        lib.vqo_gather.restype = ctypes.c_int
+        lib.vqo_gather.argtypes = [P, ctypes.c_int64, P, P]
         lib.vqo_linear.restype = ctypes.c_int
         lib.vqo_linear.argtypes = [P, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32, P]
         lib.vqo_moe_ffn.restype = ctypes.c_int
@@ -163,6 +166,17 @@ def decode(T, expert: int) -> np.ndarray:
     W = np.zeros((T.rows, T.cols), dtype=np.float32)
     _raise(_load().vqo_decode(p.ref, expert, _ptr(W)), "decode")
     return W
+
+
+def gather(T, ids: np.ndarray) -> np.ndarray:
+    """fp32 rows [n, cols]: row i is logical row ids[i] of the stacked tensor
+    (id = expert*rows + r); dead rows zero, out-of-range ids NaN."""
+    p = _Pinned(T)
+    ids = np.ascontiguousarray(ids, dtype=np.int64).ravel()
+    Y = np.zeros((len(ids), T.cols), dtype=np.float32)
+    _raise(_load().vqo_gather(p.ref, len(ids), _ptr(ids) if len(ids) else None,
+                              _ptr(Y) if len(ids) else None), "gather")
+    return Y
 
 
 def linear(T, expert: int, x: np.ndarray) -> np.ndarray:

@@ -162,44 +162,85 @@ int vqo_check(const vqo_tensor *T)
    two fp16 numbers has at most 22 significant bits and an exponent well
    inside fp32's range, so computing it in double and storing it as float is
    exact.  Skip-zero ("Qwen3.5-397B-A17B-VQ-2.4bpw: Model Card", changelog
-   2026-10-01): a dead row has no codes or scales and is exactly zero. */
+   2026-10-01): a dead row has no codes or scales and is exactly zero.
+
+   One logical row: s is its stored row (-1 = dead); writes cols floats. */
+static int decode_row(const vqo_tensor *T, int64_t s, float *wr)
+{
+    if (s < 0) {
+        for (int32_t c = 0; c < T->cols; ++c)
+            wr[c] = 0.0f;
+        return VQO_OK;
+    }
+    if (s >= T->n_stored)
+        return VQO_EMAP;
+    const int64_t wpr = vqo_words_per_row(T->cols, T->d, T->bits);
+    const int64_t groups = T->cols / 64;
+    const int64_t n_sub = T->cols / T->d;
+    const uint32_t *words = T->codes + s * wpr;
+    const uint16_t *srow = T->scales + s * groups;
+    int err = VQO_OK;
+    for (int64_t j = 0; j < n_sub; ++j) {
+        uint32_t code = vqo_code(words, T->bits, j);
+        if (code >= (uint32_t)T->K) {
+            err = VQO_ECODE;
+            code = 0;
+        }
+        double scale = vqo_half_to_double(srow[(j * T->d) / 64]);
+        for (int32_t t = 0; t < T->d; ++t) {
+            double c = vqo_half_to_double(T->codebook[(int64_t)code * T->d + t]);
+            wr[j * T->d + t] = (float)(scale * c);
+        }
+    }
+    return err;
+}
+
 int vqo_decode(const vqo_tensor *T, int32_t e, float *W)
 {
     if (!T || e < 0 || e >= T->n_experts || !W)
         return VQO_EBADARG;
-    const int64_t wpr = vqo_words_per_row(T->cols, T->d, T->bits);
-    const int64_t groups = T->cols / 64;
-    const int64_t n_sub = T->cols / T->d;
     int err = VQO_OK;
 
 #pragma omp parallel for schedule(static)
     for (int32_t r = 0; r < T->rows; ++r) {
-        float *wr = W + (int64_t)r * T->cols;
-        int64_t s = stored_row(T, e, r);
-        if (s < 0) {
+        int rc = decode_row(T, stored_row(T, e, r), W + (int64_t)r * T->cols);
+        if (rc != VQO_OK) {
+#pragma omp atomic write
+            err = rc;
+        }
+    }
+    return err;
+}
+
+/* Row gather.  Model card "Qwen3.8-Flash-Next-VQ-4.4bpw" (opening summary
+   and changelog 2026-10-04): the per-layer n-gram embedding (PLE) tables are
+   stored in the same VQ format (d=2/K=256) and read one hashed row per
+   lookup.  The tables of a stacked tensor are its experts: id = e*rows + r
+   names logical row r of table e, and Y[i] = W_e[r] in fp32 (exact, as in
+   decode_row).  The hash that produces the ids is the model's and is not
+   part of this: ids are given.  An id outside [0, n_experts*rows) has no
+   row; its output row is NaN so that the error shows. */
+int vqo_gather(const vqo_tensor *T, int64_t n, const int64_t *ids, float *Y)
+{
+    if (!T || n < 0 || (n > 0 && (!ids || !Y)))
+        return VQO_EBADARG;
+    const int64_t total = (int64_t)T->n_experts * T->rows;
+    int err = VQO_OK;
+
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float *yr = Y + i * T->cols;
+        const int64_t id = ids[i];
+        if (id < 0 || id >= total) {
             for (int32_t c = 0; c < T->cols; ++c)
-                wr[c] = 0.0f;
+                yr[c] = NAN;
             continue;
         }
-        if (s >= T->n_stored) {
+        int rc = decode_row(T, stored_row(T, (int32_t)(id / T->rows), (int32_t)(id % T->rows)),
+                            yr);
+        if (rc != VQO_OK) {
 #pragma omp atomic write
-            err = VQO_EMAP;
-            continue;
-        }
-        const uint32_t *words = T->codes + s * wpr;
-        const uint16_t *srow = T->scales + s * groups;
-        for (int64_t j = 0; j < n_sub; ++j) {
-            uint32_t code = vqo_code(words, T->bits, j);
-            if (code >= (uint32_t)T->K) {
-#pragma omp atomic write
-                err = VQO_ECODE;
-                code = 0;
-            }
-            double scale = vqo_half_to_double(srow[(j * T->d) / 64]);
-            for (int32_t t = 0; t < T->d; ++t) {
-                double c = vqo_half_to_double(T->codebook[(int64_t)code * T->d + t]);
-                wr[j * T->d + t] = (float)(scale * c);
-            }
+            err = rc;
         }
     }
     return err;

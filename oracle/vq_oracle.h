@@ -81,6 +81,11 @@ int vqo_check(const vqo_tensor *T);
 /* Decode expert e to dense fp32 W[rows][cols] (step 2). */
 int vqo_decode(const vqo_tensor *T, int32_t e, float *W);
 
+/* Y[i][:] = logical row ids[i] of the stacked tensor (id = e*rows + r), fp32,
+   for i < n; dead rows are zero, ids outside [0, n_experts*rows) give NaN
+   rows.  Y: [n][cols]. */
+int vqo_gather(const vqo_tensor *T, int64_t n, const int64_t *ids, float *Y);
+
 /* y[n][r] = sum_c W_e[r][c] * x[n][c] in fp64 (step 3).  x holds n_tok rows
    of cols values in x_dtype (VQO_X_F32 / VQO_X_BF16 bit patterns or
    VQO_X_F64 values); y is [n_tok][rows]. */

@@ -282,3 +282,83 @@ def test_moe_ffn_swapped_slots_change_output():
     y1 = oracle.moe_ffn(gate, up, down, x, ids, w)
     y2 = oracle.moe_ffn(gate, up, down, x, ids, w[:, ::-1].copy())
     assert np.abs(y1 - y2).max() > 1e-3
+
+
+# --------------------------------------------------------------------------
+# Row gather (the per-layer n-gram embedding tables of the card
+# "Qwen3.8-Flash-Next-VQ-4.4bpw" are VQ tensors at d=2/K=256 read by row).
+# --------------------------------------------------------------------------
+
+def _brute_row(T, lid):
+    """Python loops over the integer codes of one logical row (id = e*rows + r)."""
+    cb = T.codebook.view(np.float16).astype(np.float64)
+    sc = T.scales.view(np.float16).astype(np.float64)
+    s = lid if T.row_map is None else int(T.row_map[lid])
+    out = np.zeros(T.cols, dtype=np.float64)
+    if s < 0:
+        return out
+    for j in range(T.n_sub):
+        code = int(T.raw_codes[s, j])
+        for t in range(T.d):
+            out[j * T.d + t] = sc[s, (j * T.d + t) // 64] * cb[code, t]
+    return out
+
+
+@pytest.mark.parametrize("d,bits,K,dead", [(2, 8, 256, 0), (2, 8, 200, 3), (4, 9, 512, 2),
+                                           (8, 11, 2048, 0), (2, 10, 1024, 1)])
+def test_gather_brute_force_rows(d, bits, K, dead):
+    """Each gathered row equals the brute-force decode of that row, over ids in
+    random order across tables, with repeats and dead rows."""
+    rows, cols, E = 9, 192, 3
+    T = synth.make_tensor(21, d * 100 + bits, rows=rows, cols=cols, d=d, bits=bits, K=K,
+                          n_experts=E, dead_rows=dead, keep_codes=True)
+    rng = np.random.default_rng(3)
+    ids = rng.integers(0, E * rows, size=40).astype(np.int64)
+    ids[5] = ids[17]
+    Y = oracle.gather(T, ids)
+    assert Y.shape == (40, cols) and Y.dtype == np.float32
+    for i, lid in enumerate(ids):
+        assert np.array_equal(Y[i].astype(np.float64), _brute_row(T, int(lid)))
+
+
+def test_gather_equals_rows_of_decode():
+    """Gathering every logical row of every table in order rebuilds the dense
+    decode of each table, bit for bit (dead rows +0.0 included)."""
+    rows, cols, E = 7, 256, 4
+    T = synth.make_tensor(22, 1, rows=rows, cols=cols, d=2, bits=8, n_experts=E, dead_rows=2)
+    Y = oracle.gather(T, np.arange(E * rows))
+    dense = np.concatenate([oracle.decode(T, e) for e in range(E)])
+    assert np.array_equal(Y.view(np.uint32), dense.view(np.uint32))
+    dead = np.nonzero(T.row_map < 0)[0]
+    assert len(dead) == 2 * E
+    assert not Y[dead].view(np.uint32).any()          # +0.0, sign bit clear
+
+
+def test_gather_closed_form_table():
+    """Entries (k, -k/2), scale 2^-(r mod 4) per row and code j of row r equal to
+    (3j + 5r) mod 256 give W[r][2j] = (3j+5r mod 256) * 2^-(r mod 4) and
+    W[r][2j+1] = -W[r][2j]/2."""
+    rows, cols, d = 6, 128, 2
+    n_sub = cols // d
+    k = np.arange(256, dtype=np.float64)
+    cb = synth.to_half_bits(np.stack([k, -k / 2], axis=1))
+    raw = np.array([[(3 * j + 5 * r) % 256 for j in range(n_sub)] for r in range(rows)])
+    codes = synth.pack_codes(raw, 8)
+    sc = synth.to_half_bits(np.repeat((2.0 ** -(np.arange(rows) % 4))[:, None], cols // 64, 1))
+    T = synth.VQTensorHost(rows, cols, d, 8, 256, 1, cb, codes, sc, None)
+    ids = np.array([5, 0, 3, 3], dtype=np.int64)
+    Y = oracle.gather(T, ids)
+    for i, r in enumerate(ids):
+        v = ((3 * np.arange(n_sub) + 5 * r) % 256) * 2.0 ** -(r % 4)
+        assert np.array_equal(Y[i, 0::2], v.astype(np.float32))
+        assert np.array_equal(Y[i, 1::2], (-v / 2).astype(np.float32))
+
+
+def test_gather_out_of_range_ids_are_nan_rows():
+    T = synth.make_tensor(23, 1, rows=4, cols=64, d=2, bits=8, n_experts=2)
+    ids = np.array([-1, 0, 8, 7, np.iinfo(np.int64).min, 1 << 40], dtype=np.int64)
+    Y = oracle.gather(T, ids)
+    bad = [0, 2, 4, 5]
+    assert np.isnan(Y[bad]).all()
+    assert np.isfinite(Y[[1, 3]]).all()
+    assert oracle.gather(T, np.zeros(0, np.int64)).shape == (0, 64)

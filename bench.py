@@ -161,6 +161,8 @@ def main():
     torch.cuda.set_device(0)
     vq.load_library()
 
+    if args.workload in synth.GATHER_WORKLOADS:
+        return bench_gather(args, synth.GATHER_WORKLOADS[args.workload])
     wl = synth.WORKLOADS[args.workload]
     prefill = wl.n_tok > 16
     family = "prefill" if prefill else "decode"
@@ -382,6 +384,143 @@ def main():
             "layer_copies": L, "hip_graph": use_graph, "graph_replay_bit_equal": graph_check,
             "peak_frac": round(frac, 4),
             ("flops_per_step" if prefill else "bytes_per_step"): int(total / K),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_gather(args, wl):
+    """Row gather from the stacked VQ embedding tables: a step is one
+    vq_row_gather launch over one batch of ids (tokens x tables rows)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import vq_dequant_matmul_amd as vq
+
+    K = args.steps if args.steps is not None else 200
+    W = args.warmup if args.warmup is not None else 20
+    n_k = args.kernel_launches if args.kernel_launches is not None else 100
+    n_steps = K + W
+
+    t0 = time.perf_counter()
+    T = synth.make_gather_table(wl)
+    Wd = vq.VQTensor.from_host(T)
+    ids = [synth.make_gather_ids(wl, i) for i in range(n_steps)]
+    ids_dev = torch.from_numpy(np.stack(ids)).cuda()
+    y_bytes = wl.n_ids * wl.cols * 4
+    # outputs rotate over buffers that together exceed the Infinity Cache, so
+    # the stores reach HBM
+    n_out = max(2, min(16, math.ceil(4 * MALL_BYTES / y_bytes)))
+    ys = [torch.empty((wl.n_ids, wl.cols), dtype=torch.float32, device="cuda")
+          for _ in range(n_out)]
+    torch.cuda.synchronize()
+    log(f"[bench] {wl.name}: table {T.stored_bytes() / 1e9:.2f} GB, {n_steps} id batches of "
+        f"{wl.n_ids}, {n_out} output buffers, setup {time.perf_counter() - t0:.1f}s")
+
+    # algorithmic bytes: per gathered row its codes, scales, id and fp32
+    # output; per launch the codebook
+    row_bytes = T.wpr * 4 + T.groups * 2 + 8 + wl.cols * 4
+    step_bytes = wl.n_ids * row_bytes + T.K * T.d * 2
+
+    def step(i):
+        vq.vq_row_gather(Wd, ids_dev[i], out=ys[i % n_out])
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {W} steps done")
+    use_graph = not args.no_graph
+    graph = None
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(W, n_steps):
+                step(i)
+        torch.cuda.synchronize()
+
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    if use_graph:
+        graph.replay()
+    else:
+        for i in range(W, n_steps):
+            step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    log(f"[bench] timed {K} steps in {elapsed * 1e3:.2f} ms")
+
+    last = (n_steps - 1) % n_out
+    y_graph = ys[last].clone()
+    step(n_steps - 1)
+    torch.cuda.synchronize()
+    graph_check = bool(torch.equal(y_graph.view(torch.int32), ys[last].view(torch.int32)))
+    if not graph_check:
+        log("[bench] WARNING: graph replay differs from eager")
+    del y_graph
+
+    value = step_bytes * K / elapsed / 1e9
+    frac = value / HBM_PEAK_GBS
+
+    # the step is the one kernel: an event pair around n_k back-to-back
+    # launches, behind a queue of device copies that keeps the GPU busy while
+    # they are queued
+    hip = HipEvents()
+    src = torch.ones(1 << 26, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(48):
+        dst.copy_(src)
+    ev0, ev1 = hip.create(), hip.create()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    hip.record(ev0, stream)
+    for j in range(n_k):
+        step(W + (j % K))
+    hip.record(ev1, stream)
+    torch.cuda.synchronize()
+    k_mean = hip.elapsed_ms(ev0, ev1) * 1e-3 / n_k
+    hip.destroy(ev0)
+    hip.destroy(ev1)
+    del src, dst
+    achieved = step_bytes / k_mean / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": recorded_traffic(wl.name, "gather"),
+                "kernel": "vq::k_gather (row gather, exact fp32 rows)",
+                "launch_us": round(k_mean * 1e6, 2), "bytes_per_launch": int(step_bytes),
+                "timing": f"one HIP event pair around {n_k} back-to-back launches"}
+    log(f"[bench] k_gather: {k_mean * 1e6:.2f} us/launch, {achieved:.1f} GB/s")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        oracle.build(force=False)
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        t_cpu, n_cpu = 0.0, 0
+        while t_cpu < args.cpu_seconds and n_cpu < n_steps:
+            c0 = time.perf_counter()
+            oracle.gather(T, ids[W + n_cpu % K])
+            t_cpu += time.perf_counter() - c0
+            n_cpu += 1
+        cpu = {"value": round(n_cpu * step_bytes / t_cpu / 1e9, 4), "unit": "GB/s",
+               "cores": cores, "kind": "oracle",
+               "sample": f"{n_cpu} whole steps of the same workload ({wl.n_ids} rows each), "
+                         f"{t_cpu:.1f}s"}
+        log(f"[bench] cpu oracle: {n_cpu} steps in {t_cpu:.1f}s")
+
+    rec = {
+        "metric": "VQ embedding row gather GB/s (% HBM peak)", "value": round(value, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(elapsed * 1e3 / K, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16xf16->f32", "data": "synthetic",
+        "config": {
+            "workload": wl.name, "tables": wl.tables, "rows_per_table": wl.rows,
+            "cols": wl.cols, "d": wl.d, "bits": wl.bits, "K": T.K, "tokens": wl.n_tok,
+            "rows_per_step": wl.n_ids, "output_buffers": n_out, "hip_graph": use_graph,
+            "graph_replay_bit_equal": graph_check, "peak_frac": round(frac, 4),
+            "bytes_per_step": int(step_bytes),
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

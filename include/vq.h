@@ -106,6 +106,23 @@ vq_status vq_validate(const vq_tensor *W);
    to any exact decode.  w: device [rows][cols] fp32. */
 vq_status vq_dequantize(const vq_tensor *W, int32_t expert, float *w, void *stream);
 
+/* ---- row gather (VQ embedding tables) -------------------------------- */
+
+/* Card "Qwen3.8-Flash-Next-VQ-4.4bpw" (opening summary; changelog
+   2026-10-04): the per-layer n-gram embedding tables are stored in this same
+   format (d=2/K=256 there) and read one hashed row per lookup.  Here the
+   tables are the experts of W: id = e*rows + r names logical row r of table
+   e, and
+     y[i][c] = W_e[r][c] as fp32 for i < n (exact, as vq_dequantize),
+   a dead row giving +0.0 and an id outside [0, n_experts*rows) a row of NaN
+   (a bad id shows in the output; nothing outside the tensor is read).  The
+   hash that turns tokens into ids is the model's and not part of this call.
+   ids: device int64 [n], 8-byte aligned; y: device fp32 [n][cols], 16-byte
+   aligned.  n = 0 is a no-op.  Bandwidth-bound (HBM roofline, dominated by
+   the fp32 output). */
+vq_status vq_row_gather(const vq_tensor *W, int64_t n, const int64_t *ids, float *y,
+                        void *stream);
+
 /* ---- decode: one expert, a few tokens ---------------------------------- */
 
 /* y[n][r] = sum_c W_e[r][c] * x[n][c] for n < n_tokens (0..64), fp32 out.

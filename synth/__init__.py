@@ -261,3 +261,51 @@ def make_moe_inputs(wl: MoEWorkload, step: int = 0, n_experts: Optional[int] = N
     x = make_x(wl.seed, 10_000 + step, wl.n_tok, wl.hidden, "bf16")
     ids, w = make_routes(wl.seed, 20_000 + step, wl.n_tok, E, wl.top_k)
     return x, ids, w
+
+
+# --------------------------------------------------------------------------
+# Row gather from VQ embedding tables.  The card "Qwen3.8-Flash-Next-VQ-4.4bpw"
+# stores its per-layer n-gram embedding (PLE) tables at d=2/K=256 and reads
+# them by hashed row; it gives the total (51.2B parameters over its 40
+# layers) but not the table shapes.  Stand-in: one table per layer, 2^18 rows
+# of 256 columns (1.4 GB of codes for the 40 tables, several times the
+# 256 MB Infinity Cache), and one uniformly random row per (token, layer) in
+# place of the model's hash.
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class GatherWorkload:
+    name: str
+    tables: int
+    rows: int
+    cols: int
+    d: int
+    bits: int
+    n_tok: int
+    seed: int = 1240
+
+    @property
+    def n_ids(self) -> int:
+        return self.n_tok * self.tables
+
+
+GATHER_WORKLOADS = {
+    "ple_gather_d2k256_tables40_rows262144_cols256_t4096": GatherWorkload(
+        "ple_gather_d2k256_tables40_rows262144_cols256_t4096", 40, 1 << 18, 256, 2, 8, 4096),
+    "ple_gather_d2k256_tables40_rows262144_cols256_t1": GatherWorkload(
+        "ple_gather_d2k256_tables40_rows262144_cols256_t1", 40, 1 << 18, 256, 2, 8, 1),
+}
+
+
+def make_gather_table(wl: GatherWorkload) -> VQTensorHost:
+    """The stacked tables: table l is expert l of one VQ tensor."""
+    return make_tensor(wl.seed, 1, rows=wl.rows, cols=wl.cols, d=wl.d, bits=wl.bits,
+                       n_experts=wl.tables)
+
+
+def make_gather_ids(wl: GatherWorkload, step: int = 0) -> np.ndarray:
+    """int64 ids, token-major: ids[t*tables + l] = l*rows + (row of token t in
+    table l), the row uniform on [0, rows)."""
+    g = rng_for(wl.seed, 30_000 + step)
+    r = g.integers(0, wl.rows, size=(wl.n_tok, wl.tables), dtype=np.int64)
+    return np.ascontiguousarray((r + np.arange(wl.tables, dtype=np.int64) * wl.rows).ravel())

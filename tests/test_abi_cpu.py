@@ -127,3 +127,19 @@ def test_kernel_events_arguments(lib):
     assert lib.vq_set_kernel_events(None, None) == 0
     st = lib.vq_set_kernel_events(FAKE, None)
     assert st == 1 and "both" in lib.vq_last_error().decode()
+
+
+def test_row_gather_argument_errors(lib):
+    t = _t()
+    st = lib.vq_row_gather(ctypes.byref(t), -1, FAKE, FAKE, None)
+    assert st == 1 and "n = -1" in lib.vq_last_error().decode()
+    st = lib.vq_row_gather(ctypes.byref(t), 4, FAKE + 4, FAKE, None)
+    assert st == 1 and "ids" in lib.vq_last_error().decode()
+    st = lib.vq_row_gather(ctypes.byref(t), 4, FAKE, FAKE + 8, None)
+    assert st == 1 and "y:" in lib.vq_last_error().decode()
+    st = lib.vq_row_gather(ctypes.byref(t), 4, None, FAKE, None)
+    assert st == 1 and "ids" in lib.vq_last_error().decode()
+    st = lib.vq_row_gather(ctypes.byref(_t(d=3)), 4, FAKE, FAKE, None)
+    assert st == 2 and "d = 3" in lib.vq_last_error().decode()
+    # zero rows is a no-op, whatever the pointers
+    assert lib.vq_row_gather(ctypes.byref(t), 0, None, None, None) == 0

@@ -7,7 +7,7 @@ current HIP stream, allocates outputs and workspaces with torch, and raises
 HIP kernels of ``libvqmm.so``; there is no CPU or PyTorch fallback, and
 loading fails loudly when the library is missing or no GPU is present.
 
-Names follow the C ABI: ``vq_dequantize``, ``vq_expert_gemv``,
+Names follow the C ABI: ``vq_dequantize``, ``vq_row_gather``, ``vq_expert_gemv``,
 ``vq_expert_gemm``, ``vq_moe_ffn`` and their workspace-size queries.
 """
 from __future__ import annotations
@@ -67,6 +67,7 @@ def load_library():
         "vq_last_error": (ctypes.c_char_p, []),
         "vq_validate": (ctypes.c_int, [T]),
         "vq_dequantize": (ctypes.c_int, [T, I32, P, P]),
+        "vq_row_gather": (ctypes.c_int, [T, I64, P, P, P]),
         "vq_expert_gemv": (ctypes.c_int, [T, I32, I32, P, ctypes.c_int, P, P]),
         "vq_expert_gemm_workspace_size": (SZ, [T, I32]),
         "vq_expert_gemm": (ctypes.c_int, [T, I32, P, ctypes.c_int, P, P, P, SZ, P]),
@@ -199,6 +200,23 @@ def vq_dequantize(W: VQTensor, expert: int, out: Optional[torch.Tensor] = None) 
     return out
 
 
+def vq_row_gather(W: VQTensor, ids: torch.Tensor,
+                  out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rows ids[i] = e*rows + r of the stacked tensor, decoded to fp32
+    [n, cols]; dead rows +0.0, out-of-range ids NaN rows."""
+    _require_gpu()
+    lib = load_library()
+    if ids.dtype != torch.int64 or not ids.is_cuda:
+        raise TypeError("ids must be an int64 device tensor")
+    ids = ids.contiguous().view(-1)
+    n = ids.numel()
+    if out is None:
+        out = torch.empty((n, W.cols), dtype=torch.float32, device=ids.device)
+    c = W.c()
+    _check(lib.vq_row_gather(ctypes.byref(c), n, _ptr(ids), _ptr(out), _stream()))
+    return out
+
+
 def vq_expert_gemv(W: VQTensor, expert: int, x: torch.Tensor,
                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
     _require_gpu()
@@ -316,6 +334,7 @@ def vq_set_kernel_events(start, stop) -> None:
 
 __all__ = [
     "VQError", "VQTensor", "build", "load_library", "vq_validate", "vq_dequantize",
+    "vq_row_gather",
     "vq_expert_gemv", "vq_expert_gemm", "vq_expert_gemm_workspace_size", "vq_moe_ffn",
     "vq_moe_ffn_workspace_size", "vq_moe_gate_up", "vq_moe_down", "vq_moe_combine",
     "vq_set_kernel_events",

@@ -210,6 +210,31 @@ VQ_EXPORT vq_status vq_dequantize(const vq_tensor *W, int32_t expert, float *w, 
 }
 
 // ------------------------------------------------------------------------------------
+// row gather
+// ------------------------------------------------------------------------------------
+
+VQ_EXPORT vq_status vq_row_gather(const vq_tensor *W, int64_t n, const int64_t *ids, float *y,
+                                  void *stream)
+{
+    vq_status st = check_tensor(W, "W");
+    if (st != VQ_OK)
+        return st;
+    if (n < 0)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "n = %lld: must be >= 0", (long long)n);
+    if (n == 0)
+        return ok();
+    if (n > ((int64_t)1 << 40) / W->cols)
+        return fail(VQ_ERR_UNSUPPORTED, "n = %lld: output too large", (long long)n);
+    if (!ids || !aligned(ids, 8))
+        return fail(VQ_ERR_INVALID_ARGUMENT,
+                    "ids: must be a non-NULL, 8-byte aligned device pointer");
+    if (!y || !aligned(y, 16))
+        return fail(VQ_ERR_INVALID_ARGUMENT, "y: must be a non-NULL, 16-byte aligned device pointer");
+    hipError_t e = vq::launch_gather(vq::to_dev(*W), n, ids, y, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "vq_row_gather");
+}
+
+// ------------------------------------------------------------------------------------
 // decode: one expert
 // ------------------------------------------------------------------------------------
 

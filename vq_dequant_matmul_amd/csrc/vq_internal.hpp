@@ -55,6 +55,10 @@ hipError_t launch_combine(const float *z, const float *w, int n_tok, int top_k, 
 
 hipError_t launch_dequantize(const TensorDev &t, int expert, float *w, hipStream_t stream);
 
+// y[i] = logical row ids[i] (= e*rows + r) of the stacked tensor, fp32.
+hipError_t launch_gather(const TensorDev &t, int64_t n, const int64_t *ids, float *y,
+                         hipStream_t stream);
+
 // Down projection fused with the slot-ordered combine for a few tokens:
 // y[t] = sum_s w[t][s] * W_down_{e[t][s]} h[t*top_k + s].  mix_supported()
 // tells whether the shapes fit the fused kernel.

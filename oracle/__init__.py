@@ -87,6 +87,9 @@ def _load():
         lib.vqo_moe_ffn.restype = ctypes.c_int
         lib.vqo_moe_ffn.argtypes = [P, P, P, ctypes.c_int32, ctypes.c_int32, P, ctypes.c_int32,
                                     P, P, ctypes.c_int32, P, P]
+        lib.vqo_moe_stack.restype = ctypes.c_int
+        lib.vqo_moe_stack.argtypes = [ctypes.c_int32, P, P, P, ctypes.c_int32, ctypes.c_int32,
+                                      P, P, P]
         lib.vqo_swiglu.restype = ctypes.c_double
         lib.vqo_swiglu.argtypes = [ctypes.c_double, ctypes.c_double]
         _lib = lib
@@ -206,6 +209,29 @@ def moe_ffn(gate, up, down, x: np.ndarray, ids: np.ndarray, weights: np.ndarray,
                              _ptr(ids), _ptr(w), len(tokens), _ptr(tokens), _ptr(y))
     _raise(rc, "moe_ffn")
     return y
+
+
+def moe_stack(layers, x: np.ndarray) -> np.ndarray:
+    """fp64 hidden state after h <- h + FFN_l(h) over the layers (gate, up,
+    down, ids, weights), starting from x [n_tok, hidden] (any float dtype)."""
+    h = np.ascontiguousarray(x, dtype=np.float64).copy()
+    n_tok = h.shape[0]
+    L = len(layers)
+    pins = [(_Pinned(g), _Pinned(u), _Pinned(d)) for g, u, d, _, _ in layers]
+    ids = [np.ascontiguousarray(l[3], dtype=np.int32) for l in layers]
+    ws = [np.ascontiguousarray(l[4], dtype=np.float32) for l in layers]
+    top_k = ids[0].shape[1] if L else 1
+    TP = ctypes.POINTER(_Tensor)
+    arr = lambda k: (TP * max(L, 1))(*[ctypes.pointer(p[k].struct) for p in pins])
+    ga, ua, da = arr(0), arr(1), arr(2)
+    ia = (ctypes.c_void_p * max(L, 1))(*[a.ctypes.data for a in ids])
+    wa = (ctypes.c_void_p * max(L, 1))(*[a.ctypes.data for a in ws])
+    rc = _load().vqo_moe_stack(L, ctypes.cast(ga, ctypes.c_void_p), ctypes.cast(ua, ctypes.c_void_p),
+                               ctypes.cast(da, ctypes.c_void_p), n_tok, top_k,
+                               ctypes.cast(ia, ctypes.c_void_p), ctypes.cast(wa, ctypes.c_void_p),
+                               _ptr(h))
+    _raise(rc, "moe_stack")
+    return h
 
 
 def swiglu(g: float, u: float) -> float:

@@ -393,3 +393,49 @@ int vqo_moe_ffn(const vqo_tensor *gate, const vqo_tensor *up, const vqo_tensor *
     free(h);
     return err;
 }
+
+/* ---------------------------------------------------------------------- */
+/* Step 5: a stack of MoE layers                                           */
+/* ---------------------------------------------------------------------- */
+
+/* Layers in sequence, each applying its own routed FFN (step 4) to the
+   running hidden state and adding the result to it:
+       h <- h + FFN_l(h)   for l = 0, 1, ..., n_layers-1.
+   The cards build models whose expert layers differ in geometry (promoted
+   layers: "GLM-5.3-Flash-VQ-2.7bpw" and "Qwen3.8-Flash-Next-VQ-4.4bpw",
+   opening summaries); a layer's FFN is computed exactly as in step 4, from
+   the fp64 state.  The residual form is the standard place of an MoE block
+   in a decoder layer (the cards do not describe the block); the attention,
+   norms and router between the blocks are not modelled.  h: [n_tok][hidden]
+   fp64, updated in place. */
+int vqo_moe_stack(int32_t n_layers, const vqo_tensor *const *gate,
+                  const vqo_tensor *const *up, const vqo_tensor *const *down,
+                  int32_t n_tok, int32_t top_k, const int32_t *const *ids,
+                  const float *const *w, double *h)
+{
+    if (n_layers < 0 || n_tok < 0 || (n_layers > 0 && (!gate || !up || !down || !ids || !w)))
+        return VQO_EBADARG;
+    if (n_layers == 0 || n_tok == 0)
+        return VQO_OK;
+    if (!h)
+        return VQO_EBADARG;
+    const int32_t hidden = gate[0]->cols;
+    int32_t *tokens = (int32_t *)malloc(sizeof(int32_t) * (size_t)n_tok);
+    double *y = (double *)malloc(sizeof(double) * (size_t)n_tok * hidden);
+    int err = (tokens && y) ? VQO_OK : VQO_ENOMEM;
+    for (int32_t t = 0; t < n_tok && tokens; ++t)
+        tokens[t] = t;
+    for (int32_t l = 0; l < n_layers && err == VQO_OK; ++l) {
+        if (!gate[l] || gate[l]->cols != hidden) {
+            err = VQO_EBADARG;
+            break;
+        }
+        err = vqo_moe_ffn(gate[l], up[l], down[l], n_tok, top_k, h, VQO_X_F64, ids[l], w[l],
+                          n_tok, tokens, y);
+        for (int64_t i = 0; i < (int64_t)n_tok * hidden && err == VQO_OK; ++i)
+            h[i] += y[i];
+    }
+    free(tokens);
+    free(y);
+    return err;
+}

@@ -103,6 +103,15 @@ int vqo_moe_ffn(const vqo_tensor *gate, const vqo_tensor *up, const vqo_tensor *
 /* SwiGLU activation product silu(g) * u with silu(z) = z / (1 + exp(-z)). */
 double vqo_swiglu(double g, double u);
 
+/* A stack of MoE layers (step 5): h <- h + FFN_l(h) for l = 0..n_layers-1,
+   FFN_l as in vqo_moe_ffn over all tokens, with layer l's tensors and
+   routing (ids[l], w[l]: [n_tok][top_k]).  h: [n_tok][hidden] fp64, in
+   place. */
+int vqo_moe_stack(int32_t n_layers, const vqo_tensor *const *gate,
+                  const vqo_tensor *const *up, const vqo_tensor *const *down,
+                  int32_t n_tok, int32_t top_k, const int32_t *const *ids,
+                  const float *const *w, double *h);
+
 #ifdef __cplusplus
 }
 #endif

@@ -362,3 +362,66 @@ def test_gather_out_of_range_ids_are_nan_rows():
     assert np.isnan(Y[bad]).all()
     assert np.isfinite(Y[[1, 3]]).all()
     assert oracle.gather(T, np.zeros(0, np.int64)).shape == (0, 64)
+
+
+# --------------------------------------------------------------------------
+# A stack of MoE layers on a residual stream, layers of mixed geometry (the
+# promoted layers of "GLM-5.3-Flash-VQ-2.7bpw" and
+# "Qwen3.8-Flash-Next-VQ-4.4bpw").
+# --------------------------------------------------------------------------
+
+def _stack_layer(seed, d, bits, hidden=128, inter=64, E=6, top_k=2, n_tok=3, dead=0,
+                 zero_w=False):
+    G = synth.make_tensor(seed, 1, rows=inter, cols=hidden, d=d, bits=bits, n_experts=E,
+                          dead_rows=dead)
+    U = synth.make_tensor(seed, 2, rows=inter, cols=hidden, d=d, bits=bits, n_experts=E,
+                          dead_rows=dead)
+    D = synth.make_tensor(seed, 3, rows=hidden, cols=inter, d=d, bits=bits, n_experts=E,
+                          dead_rows=dead)
+    ids, w = synth.make_routes(seed, 4, n_tok, E, top_k)
+    if zero_w:
+        w = np.zeros_like(w)
+    return (G, U, D, ids, w)
+
+
+def _x64(n_tok=3, hidden=128):
+    return synth.make_x(60, 1, n_tok, hidden, "f32").astype(np.float64)
+
+
+def test_stack_one_layer_is_residual_plus_ffn():
+    A = _stack_layer(61, 4, 9)
+    x = _x64()
+    assert np.array_equal(oracle.moe_stack([A], x), x + oracle.moe_ffn(*A[:3], x, A[3], A[4]))
+
+
+def test_stack_identity_layers():
+    """A layer whose down projection is all dead, or whose gate weights are
+    all zero, adds exactly nothing; inserting it changes no bit."""
+    A, B = _stack_layer(62, 4, 9), _stack_layer(63, 2, 8)
+    dead = _stack_layer(64, 4, 11, dead=0)
+    dead = (dead[0], dead[1], synth.make_tensor(64, 3, rows=128, cols=64, d=4, bits=11,
+                                                n_experts=6, dead_rows=128), dead[3], dead[4])
+    zw = _stack_layer(65, 2, 10, zero_w=True)
+    x = _x64()
+    ref = oracle.moe_stack([A, B], x)
+    assert np.array_equal(oracle.moe_stack([A, dead, B], x), ref)
+    assert np.array_equal(oracle.moe_stack([zw, A, B, zw], x), ref)
+    assert np.array_equal(oracle.moe_stack([dead, zw], x), x)
+    assert np.array_equal(oracle.moe_stack([], x), x)
+
+
+def test_stack_zero_state_stays_zero():
+    """silu(0) * 0 = 0: from h = 0 every layer adds exact zeros."""
+    layers = [_stack_layer(66 + i, d, b) for i, (d, b) in enumerate([(4, 9), (2, 8), (4, 11)])]
+    x = np.zeros((3, 128))
+    assert not oracle.moe_stack(layers, x).any()
+
+
+def test_stack_layer_order_matters():
+    A, B = _stack_layer(70, 4, 9), _stack_layer(71, 2, 10)
+    x = _x64()
+    ab, ba = oracle.moe_stack([A, B], x), oracle.moe_stack([B, A], x)
+    assert not np.allclose(ab, ba, rtol=1e-6, atol=0)
+    # and the second layer sees the first layer's output, not x
+    h1 = oracle.moe_stack([A], x)
+    assert np.array_equal(ab, h1 + oracle.moe_ffn(*B[:3], h1, B[3], B[4]))

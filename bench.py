@@ -163,6 +163,8 @@ def main():
 
     if args.workload in synth.GATHER_WORKLOADS:
         return bench_gather(args, synth.GATHER_WORKLOADS[args.workload])
+    if args.workload in synth.STACK_WORKLOADS:
+        return bench_stack(args, synth.STACK_WORKLOADS[args.workload])
     wl = synth.WORKLOADS[args.workload]
     prefill = wl.n_tok > 16
     family = "prefill" if prefill else "decode"
@@ -384,6 +386,183 @@ def main():
             "layer_copies": L, "hip_graph": use_graph, "graph_replay_bit_equal": graph_check,
             "peak_frac": round(frac, 4),
             ("flops_per_step" if prefill else "bytes_per_step"): int(total / K),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_stack(args, sw):
+    """One token through a stack of MoE layers with promoted layers: a step
+    is one vq_moe_stack call (every layer's gate+up and down+combine, the
+    hidden state updated in place) from a fresh hidden state and fresh
+    routes for every layer."""
+    import numpy as np
+    import torch
+
+    import synth
+    import vq_dequant_matmul_amd as vq
+
+    b = sw.base
+    K = args.steps if args.steps is not None else 30
+    W = args.warmup if args.warmup is not None else 3
+    n_k = args.kernel_launches if args.kernel_launches is not None else 200
+    n_steps = K + W
+
+    t0 = time.perf_counter()
+    # one host layer per geometry; every position of the stack gets a device
+    # copy at its own address, with enough copies per geometry that a copy
+    # is reused only after several times the Infinity Cache has streamed by
+    geoms = sorted({sw.layer_bits(l) for l in range(sw.n_layers)})
+    host = {bits: synth.make_stack_layer(
+        sw, next(l for l in range(sw.n_layers) if sw.layer_bits(l) == bits)) for bits in geoms}
+    layer_bytes = {bits: sum(t.stored_bytes() for t in host[bits]) for bits in geoms}
+    copies = {bits: max(2, min(sum(sw.layer_bits(l) == bits for l in range(sw.n_layers)),
+                               math.ceil(4 * MALL_BYTES / layer_bytes[bits])))
+              for bits in geoms}
+    dev = {bits: [[vq.VQTensor.from_host(t) for t in host[bits]]] for bits in geoms}
+    for bits in geoms:
+        dev[bits] += [[t.clone() for t in dev[bits][0]] for _ in range(copies[bits] - 1)]
+    pos = {bits: 0 for bits in geoms}
+    stack = []
+    for l in range(sw.n_layers):
+        bits = sw.layer_bits(l)
+        stack.append(dev[bits][pos[bits] % copies[bits]])
+        pos[bits] += 1
+    xs, ids, ws = [], [], []
+    for i in range(n_steps):
+        x, r, w = synth.make_stack_inputs(sw, i)
+        xs.append(x)
+        ids.append(r)
+        ws.append(w)
+    x_dev = torch.from_numpy(np.stack(xs)).cuda()
+    ids_dev = torch.from_numpy(np.stack(ids)).cuda()
+    w_dev = torch.from_numpy(np.stack(ws)).cuda()
+    hidden = torch.empty((b.n_tok, b.hidden), dtype=torch.float32, device="cuda")
+
+    def layers_of(i):
+        return [(*stack[l], ids_dev[i, l], w_dev[i, l]) for l in range(sw.n_layers)]
+    step_layers = [layers_of(i) for i in range(n_steps)]
+    ws_bytes = vq.vq_moe_stack_workspace_size(step_layers[0], b.n_tok, b.top_k)
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] {sw.name}: geometries {geoms} with {copies} device copies, "
+        f"{sum(layer_bytes[g] * copies[g] for g in geoms) / 1e9:.2f} GB of layers, "
+        f"setup {time.perf_counter() - t0:.1f}s")
+
+    hl = {bits: host[bits] for bits in geoms}
+    io_bytes = b.n_tok * b.hidden * 4 * 3 + b.n_tok * b.top_k * 8
+
+    def layer_bytes_of(i, l, projs=3):
+        G, U, D = hl[sw.layer_bits(l)]
+        uniq = np.unique(ids[i][l])
+        ts = (G, U, D)[:projs]
+        return int(sum(expert_bytes(t, int(e)) for e in uniq for t in ts)
+                   + sum(t.K * t.d * 2 for t in ts) + io_bytes)
+
+    def step_bytes(i):
+        return sum(layer_bytes_of(i, l) for l in range(sw.n_layers))
+
+    def step(i):
+        hidden.copy_(x_dev[i])
+        vq.vq_moe_stack(step_layers[i], hidden, workspace=workspace)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {W} steps done")
+    use_graph = not args.no_graph
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(W, n_steps):
+                step(i)
+        torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    if use_graph:
+        graph.replay()
+    else:
+        for i in range(W, n_steps):
+            step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    log(f"[bench] timed {K} steps in {elapsed * 1e3:.2f} ms")
+    h_graph = hidden.clone()
+    step(n_steps - 1)
+    torch.cuda.synchronize()
+    graph_check = bool(torch.equal(h_graph.view(torch.int32), hidden.view(torch.int32)))
+    if not graph_check:
+        log("[bench] WARNING: graph replay differs from eager")
+    total = sum(step_bytes(i) for i in range(W, n_steps))
+    value = total / elapsed / 1e9
+
+    # dominant kernel: the gate+up launch, over the stack's layers in order
+    hip = HipEvents()
+    src = torch.ones(1 << 26, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    h = torch.empty((b.n_tok * b.top_k, b.inter), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(48):
+        dst.copy_(src)
+    ev0, ev1 = hip.create(), hip.create()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    hip.record(ev0, stream)
+    for j in range(n_k):
+        i, l = W + (j // sw.n_layers) % K, j % sw.n_layers
+        G, U, _ = stack[l]
+        vq.vq_moe_gate_up(G, U, x_dev[i], ids_dev[i, l], out=h)
+    hip.record(ev1, stream)
+    torch.cuda.synchronize()
+    k_mean = hip.elapsed_ms(ev0, ev1) * 1e-3 / n_k
+    hip.destroy(ev0)
+    hip.destroy(ev1)
+    del src, dst, h
+    kwork = np.array([layer_bytes_of(W + (j // sw.n_layers) % K, j % sw.n_layers, 2)
+                      - b.n_tok * b.hidden * 8 + b.n_tok * b.top_k * b.inter * 4
+                      for j in range(n_k)])
+    achieved = float(kwork.mean() / k_mean / 1e9)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None,
+                "kernel": "vq::k_rows (gate+up+SwiGLU, fused), over the stack's layers",
+                "launch_us": round(k_mean * 1e6, 2), "bytes_per_launch": int(kwork.mean()),
+                "timing": f"one HIP event pair around {n_k} back-to-back launches"}
+    log(f"[bench] gate+up: {k_mean * 1e6:.2f} us/launch, {achieved:.1f} GB/s")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        oracle.build(force=False)
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        t_cpu, n_cpu, work = 0.0, 0, 0
+        while t_cpu < args.cpu_seconds and n_cpu < K:
+            i = W + n_cpu
+            layers = [(*hl[sw.layer_bits(l)], ids[i][l], ws[i][l]) for l in range(sw.n_layers)]
+            c0 = time.perf_counter()
+            oracle.moe_stack(layers, xs[i])
+            t_cpu += time.perf_counter() - c0
+            work += step_bytes(i)
+            n_cpu += 1
+        cpu = {"value": round(work / t_cpu / 1e9, 4), "unit": "GB/s", "cores": cores,
+               "kind": "oracle",
+               "sample": f"{n_cpu} whole steps of the same workload ({sw.n_layers} layers), "
+                         f"{t_cpu:.1f}s"}
+        log(f"[bench] cpu oracle: {n_cpu} steps in {t_cpu:.1f}s")
+
+    rec = {
+        "metric": "VQ MoE layer stack GB/s (decode, % HBM peak)", "value": round(value, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(elapsed * 1e3 / K, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16xf16->f32", "data": "synthetic",
+        "config": {
+            "workload": sw.name, "layers": sw.n_layers, "promoted_layers": list(sw.promoted),
+            "experts": b.n_experts, "top_k": b.top_k, "hidden": b.hidden, "inter": b.inter,
+            "d": b.d, "bits": b.bits, "promoted_bits": sw.promoted_bits, "tokens": b.n_tok,
+            "device_copies": {str(k): v for k, v in copies.items()}, "hip_graph": use_graph,
+            "graph_replay_bit_equal": graph_check,
+            "peak_frac": round(value / HBM_PEAK_GBS, 4), "bytes_per_step": int(total / K),
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

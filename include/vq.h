@@ -186,6 +186,37 @@ vq_status vq_moe_down(const vq_tensor *down, int32_t n_tokens, int32_t top_k, co
 vq_status vq_moe_combine(int32_t n_tokens, int32_t top_k, int32_t hidden, const float *z,
                          const float *topk_weights, float *y, void *stream);
 
+/* ---- a stack of MoE layers on a residual stream (small batches) ---------- */
+
+/* Decode through several MoE layers in one call.  Layers may differ in
+   geometry (d, bits, K) and in inter size, as the promoted layers do on
+   the cards "GLM-5.3-Flash-VQ-2.7bpw" (opening summary: eight layers at
+   d=4/K=2048 among d=4/K=512 ones) and "Qwen3.8-Flash-Next-VQ-4.4bpw"
+   (opening summary: seven layers at d=2/K=1024 among d=2/K=256 ones); they
+   share hidden size and top_k.  Each
+   layer brings its own routing (topk_ids, topk_weights: device
+   [n_tokens][top_k], as for vq_moe_ffn).  For l = 0 .. n_layers-1, in order:
+     hidden[t] <- hidden[t] + FFN_l(hidden[t])      (FFN_l as in vq_moe_ffn)
+   hidden: device fp32 [n_tokens][hidden size], 16-byte aligned, read and
+   updated in place.  The router, attention and norms between the MoE blocks
+   are not part of this call.  n_tokens <= 16 (the decode kernels, two
+   launches per layer; capture the call in a HIP graph to replay a step).
+   workspace: device, at least vq_moe_stack_workspace_size() bytes, 256-byte
+   aligned; shared by the layers in turn. */
+typedef struct vq_moe_layer {
+    const vq_tensor *gate;       /* rows = inter, cols = hidden size        */
+    const vq_tensor *up;         /* same shape, d and bits as gate           */
+    const vq_tensor *down;       /* rows = hidden size, cols = inter         */
+    const int32_t *topk_ids;     /* device int32 [n_tokens][top_k]           */
+    const float *topk_weights;   /* device fp32 [n_tokens][top_k]            */
+} vq_moe_layer;
+
+size_t vq_moe_stack_workspace_size(const vq_moe_layer *layers, int32_t n_layers,
+                                   int32_t n_tokens, int32_t top_k);
+vq_status vq_moe_stack(const vq_moe_layer *layers, int32_t n_layers, int32_t n_tokens,
+                       int32_t top_k, float *hidden, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
 /* ---- measurement -------------------------------------------------------------- */
 
 /* Until cleared (NULL, NULL), every vq_moe_ffn / vq_moe_gate_up /

@@ -128,7 +128,7 @@ def _padding_mask(n_sub: int, bits: int) -> Optional[np.ndarray]:
 
 def make_tensor(seed: int, stream: int, *, rows: int, cols: int, d: int, bits: int,
                 K: Optional[int] = None, n_experts: int = 1, dead_rows: int = 0,
-                keep_codes: bool = False) -> VQTensorHost:
+                keep_codes: bool = False, scale_range=(0.01, 0.05)) -> VQTensorHost:
     """A seeded VQ tensor.  ``dead_rows`` rows of every expert are dead
     (skip-zero).  ``keep_codes`` also returns the integer codes."""
     K = (1 << bits) if K is None else K
@@ -155,7 +155,7 @@ def make_tensor(seed: int, stream: int, *, rows: int, cols: int, d: int, bits: i
             nxt += len(idx)
         n_stored = nxt
 
-    scales = to_half_bits(g_sc.uniform(0.01, 0.05, size=(n_stored, cols // 64)))
+    scales = to_half_bits(g_sc.uniform(*scale_range, size=(n_stored, cols // 64)))
     n_sub = cols // d
     wpr = words_per_row(cols, d, bits)
     raw = None
@@ -242,7 +242,8 @@ WORKLOADS = {
 LINEAR_256x512 = dict(rows=256, cols=512, d=2, bits=8, n_experts=1, seed=1233)
 
 
-def make_moe_layer(wl: MoEWorkload, layer: int = 0, n_experts: Optional[int] = None):
+def make_moe_layer(wl: MoEWorkload, layer: int = 0, n_experts: Optional[int] = None,
+                   down_scale_range=(0.01, 0.05)):
     """gate, up, down tensors of one MoE layer (one codebook per projection,
     shared by the layer's experts)."""
     E = wl.n_experts if n_experts is None else n_experts
@@ -251,7 +252,8 @@ def make_moe_layer(wl: MoEWorkload, layer: int = 0, n_experts: Optional[int] = N
     up = make_tensor(wl.seed, 100 * layer + 2, rows=wl.inter, cols=wl.hidden, d=wl.d,
                      bits=wl.bits, n_experts=E, dead_rows=wl.dead_rows(wl.inter))
     down = make_tensor(wl.seed, 100 * layer + 3, rows=wl.hidden, cols=wl.inter, d=wl.d,
-                       bits=wl.bits, n_experts=E, dead_rows=wl.dead_rows(wl.hidden))
+                       bits=wl.bits, n_experts=E, dead_rows=wl.dead_rows(wl.hidden),
+                       scale_range=down_scale_range)
     return gate, up, down
 
 
@@ -309,3 +311,68 @@ def make_gather_ids(wl: GatherWorkload, step: int = 0) -> np.ndarray:
     g = rng_for(wl.seed, 30_000 + step)
     r = g.integers(0, wl.rows, size=(wl.n_tok, wl.tables), dtype=np.int64)
     return np.ascontiguousarray((r + np.arange(wl.tables, dtype=np.int64) * wl.rows).ravel())
+
+
+# --------------------------------------------------------------------------
+# Stacks of MoE layers with promoted layers.  "GLM-5.3-Flash-VQ-2.7bpw" keeps
+# its experts at d=4/K=512 and promotes layers 20, 27, 29, 31, 33, 34, 35 and
+# 39 to d=4/K=2048; "Qwen3.8-Flash-Next-VQ-4.4bpw" keeps d=2/K=256 and
+# promotes layers 0, 1, 2, 16, 24, 31 and 39 to d=2/K=1024 (both opening
+# summaries).  40 layers as on those cards; the layer shapes are the decode
+# workloads' above.  A layer adds its FFN output to the running state, and an
+# FFN of random weights grows about quadratically with its input, so forty
+# of them at the experts' usual scales overflow fp32.  In the stacks the down
+# projections' scales are drawn 64 times smaller (U(0.01, 0.05) / 64), which
+# keeps the state bounded over 40 layers (the layers then change it by 8 %
+# and 14 % in L2 for the two stacks below); a real model bounds it with the
+# norms between blocks, which are not part of this path.
+# --------------------------------------------------------------------------
+
+STACK_DOWN_SCALES = (0.01 / 64, 0.05 / 64)
+
+@dataclass(frozen=True)
+class StackWorkload:
+    name: str
+    n_layers: int
+    promoted: tuple
+    base: MoEWorkload          # shapes, routing and the base geometry
+    promoted_bits: int         # same d, wider code
+
+    def layer_bits(self, layer: int) -> int:
+        return self.promoted_bits if layer in self.promoted else self.base.bits
+
+    def layer_workload(self, layer: int) -> MoEWorkload:
+        b = self.base
+        bits = self.layer_bits(layer)
+        return MoEWorkload(f"{self.name}_l{layer}", b.n_experts, b.top_k, b.hidden, b.inter,
+                           b.d, bits, b.n_tok, b.dead_frac, b.seed + (17 if bits != b.bits else 0))
+
+
+STACK_WORKLOADS = {
+    "moe_stack40_e128_h2048_i768_d4k512_p8k2048_b1": StackWorkload(
+        "moe_stack40_e128_h2048_i768_d4k512_p8k2048_b1", 40, (20, 27, 29, 31, 33, 34, 35, 39),
+        WORKLOADS["moe_decode_e128_h2048_i768_d4k512_b1"], 11),
+    "moe_stack40_e512_h4096_i1024_d2k256_p7k1024_b1": StackWorkload(
+        "moe_stack40_e512_h4096_i1024_d2k256_p7k1024_b1", 40, (0, 1, 2, 16, 24, 31, 39),
+        WORKLOADS["moe_decode_e512_h4096_i1024_d2k256_b1"], 10),
+}
+
+
+def make_stack_inputs(sw: StackWorkload, step: int = 0, n_experts: Optional[int] = None):
+    """The step's hidden state (float32 [n_tok, hidden]) and every layer's
+    routes (ids int32 [n_layers, n_tok, top_k], weights float32 alike)."""
+    b = sw.base
+    E = b.n_experts if n_experts is None else n_experts
+    x = make_x(b.seed, 40_000 + step, b.n_tok, b.hidden, "f32")
+    ids, ws = [], []
+    for layer in range(sw.n_layers):
+        i, w = make_routes(b.seed, 50_000 + 1000 * step + layer, b.n_tok, E, b.top_k)
+        ids.append(i)
+        ws.append(w)
+    return x, np.stack(ids), np.stack(ws)
+
+
+def make_stack_layer(sw: StackWorkload, layer: int):
+    """gate, up, down of stack layer `layer` (layers of one geometry share
+    their values)."""
+    return make_moe_layer(sw.layer_workload(layer), down_scale_range=STACK_DOWN_SCALES)

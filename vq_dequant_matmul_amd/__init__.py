@@ -42,6 +42,14 @@ class _CTensor(ctypes.Structure):
     ]
 
 
+class _CLayer(ctypes.Structure):
+    _fields_ = [
+        ("gate", ctypes.POINTER(_CTensor)), ("up", ctypes.POINTER(_CTensor)),
+        ("down", ctypes.POINTER(_CTensor)),
+        ("topk_ids", ctypes.c_void_p), ("topk_weights", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -77,6 +85,8 @@ def load_library():
         "vq_moe_down": (ctypes.c_int, [T, I32, I32, P, P, P, P]),
         "vq_moe_combine": (ctypes.c_int, [I32, I32, I32, P, P, P, P]),
         "vq_set_kernel_events": (ctypes.c_int, [P, P]),
+        "vq_moe_stack_workspace_size": (SZ, [ctypes.POINTER(_CLayer), I32, I32, I32]),
+        "vq_moe_stack": (ctypes.c_int, [ctypes.POINTER(_CLayer), I32, I32, I32, P, P, SZ, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -283,6 +293,47 @@ def vq_moe_ffn(gate: VQTensor, up: VQTensor, down: VQTensor, x: torch.Tensor,
     return out
 
 
+class _StackArgs:
+    """The C layer array and the descriptors it points at, kept alive together."""
+
+    def __init__(self, layers):
+        self.tensors = []
+        self.arr = (_CLayer * max(len(layers), 1))()
+        for i, (g, u, d, ids, w) in enumerate(layers):
+            if ids.dtype != torch.int32 or w.dtype != torch.float32:
+                raise TypeError("topk_ids must be int32 and topk_weights float32")
+            if not (ids.is_contiguous() and w.is_contiguous()):
+                raise ValueError("topk_ids and topk_weights must be contiguous")
+            cs = (g.c(), u.c(), d.c())
+            self.tensors.append(cs)
+            self.arr[i] = _CLayer(ctypes.pointer(cs[0]), ctypes.pointer(cs[1]),
+                                  ctypes.pointer(cs[2]), ids.data_ptr(), w.data_ptr())
+
+
+def vq_moe_stack_workspace_size(layers, n_tokens: int, top_k: int) -> int:
+    a = _StackArgs(layers)
+    return int(load_library().vq_moe_stack_workspace_size(a.arr, len(layers), n_tokens, top_k))
+
+
+def vq_moe_stack(layers, hidden: torch.Tensor,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """hidden <- hidden + FFN_l(hidden) for each layer (gate, up, down,
+    topk_ids, topk_weights) in order; fp32 [n_tokens, hidden], in place."""
+    _require_gpu()
+    lib = load_library()
+    if hidden.dtype != torch.float32 or not hidden.is_contiguous():
+        raise TypeError("hidden must be a contiguous float32 device tensor")
+    n = hidden.shape[0]
+    k = layers[0][3].shape[1] if layers else 1
+    a = _StackArgs(layers)
+    if workspace is None:
+        ws = lib.vq_moe_stack_workspace_size(a.arr, len(layers), n, k)
+        workspace = torch.empty(max(int(ws), 1), dtype=torch.uint8, device=hidden.device)
+    _check(lib.vq_moe_stack(a.arr, len(layers), n, k, _ptr(hidden), _ptr(workspace),
+                            workspace.numel(), _stream()))
+    return hidden
+
+
 def vq_moe_gate_up(gate: VQTensor, up: VQTensor, x: torch.Tensor, topk_ids: torch.Tensor,
                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """h[t*top_k + s] = silu(W_gate_e x_t) * (W_up_e x_t), e = topk_ids[t, s]."""
@@ -337,6 +388,6 @@ __all__ = [
     "vq_row_gather",
     "vq_expert_gemv", "vq_expert_gemm", "vq_expert_gemm_workspace_size", "vq_moe_ffn",
     "vq_moe_ffn_workspace_size", "vq_moe_gate_up", "vq_moe_down", "vq_moe_combine",
-    "vq_set_kernel_events",
+    "vq_set_kernel_events", "vq_moe_stack", "vq_moe_stack_workspace_size",
     "VQ_F32", "VQ_BF16",
 ]

@@ -7,6 +7,7 @@
 // preconditions in vq.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -407,6 +408,31 @@ static vq_status check_ffn(const vq_tensor *gate, const vq_tensor *up, const vq_
     return VQ_OK;
 }
 
+// The small-batch FFN: gate+up+SwiGLU -> down -> slot-ordered combine, into y
+// (accumulate: added to y).  Sizes and the workspace are checked by the caller.
+static vq_status run_decode_ffn(const vq::TensorDev &g, const vq::TensorDev &u,
+                                const vq::TensorDev &dn, int n_tokens, int top_k, const void *x,
+                                bool x_f32, const int32_t *ids, const float *w, float *y,
+                                bool accumulate, const DecodeWs &ws, void *workspace,
+                                hipStream_t s, const char *what)
+{
+    float *h = reinterpret_cast<float *>(static_cast<char *>(workspace) + ws.h_off);
+    float *z = reinterpret_cast<float *>(static_cast<char *>(workspace) + ws.z_off);
+    hipError_t e = launch_gate_up(g, u, n_tokens, top_k, x, x_f32, ids, h, s);
+    if (e != hipSuccess)
+        return hip_fail(e, what);
+    if (vq::mix_supported(dn, n_tokens, top_k)) {
+        // down projection and combine in one pass over the output rows
+        e = vq::launch_mix(dn, n_tokens, top_k, h, ids, w, y, accumulate, s);
+        return e == hipSuccess ? ok() : hip_fail(e, what);
+    }
+    e = launch_down(dn, n_tokens, top_k, h, ids, z, s);
+    if (e != hipSuccess)
+        return hip_fail(e, what);
+    e = vq::launch_combine(z, w, n_tokens, top_k, dn.rows, y, accumulate, s);
+    return e == hipSuccess ? ok() : hip_fail(e, what);
+}
+
 VQ_EXPORT size_t vq_moe_ffn_workspace_size(const vq_tensor *gate, const vq_tensor *up,
                                            const vq_tensor *down, int32_t n_tokens, int32_t top_k)
 {
@@ -460,21 +486,83 @@ VQ_EXPORT vq_status vq_moe_ffn(const vq_tensor *gate, const vq_tensor *up, const
         return fail(VQ_ERR_WORKSPACE,
                     "workspace: need %zu bytes, 256-byte aligned (got %zu bytes at %p)", ws.total,
                     workspace_bytes, workspace);
-    float *h = reinterpret_cast<float *>(static_cast<char *>(workspace) + ws.h_off);
-    float *z = reinterpret_cast<float *>(static_cast<char *>(workspace) + ws.z_off);
-    hipError_t e = launch_gate_up(g, u, n_tokens, top_k, x, x_dtype == VQ_F32, topk_ids, h, s);
-    if (e != hipSuccess)
-        return hip_fail(e, "vq_moe_ffn (gate/up)");
-    if (vq::mix_supported(dn, n_tokens, top_k)) {
-        // down projection and combine in one pass over the output rows
-        e = vq::launch_mix(dn, n_tokens, top_k, h, topk_ids, topk_weights, y, s);
-        return e == hipSuccess ? ok() : hip_fail(e, "vq_moe_ffn (down+combine)");
+    return run_decode_ffn(g, u, dn, n_tokens, top_k, x, x_dtype == VQ_F32, topk_ids,
+                          topk_weights, y, false, ws, workspace, s, "vq_moe_ffn (decode)");
+}
+
+// ------------------------------------------------------------------------------------
+// a stack of MoE layers on a residual stream (small batches)
+// ------------------------------------------------------------------------------------
+
+static vq_status check_stack(const vq_moe_layer *layers, int32_t n_layers, int32_t n_tokens,
+                             int32_t top_k)
+{
+    if (n_layers < 0 || (n_layers > 0 && !layers))
+        return fail(VQ_ERR_INVALID_ARGUMENT, "n_layers = %d: must be >= 0 with a layer array",
+                    n_layers);
+    if (n_tokens < 0 || n_tokens > kDecodeMaxTokens)
+        return fail(VQ_ERR_UNSUPPORTED, "n_tokens = %d: the layer stack takes 0..%d tokens",
+                    n_tokens, kDecodeMaxTokens);
+    for (int32_t l = 0; l < n_layers; ++l) {
+        const vq_moe_layer &L = layers[l];
+        vq_status st = check_ffn(L.gate, L.up, L.down, n_tokens, top_k);
+        if (st != VQ_OK)
+            return fail(st, "layer %d: %s", l, vq_last_error());
+        if (L.gate->cols != layers[0].gate->cols)
+            return fail(VQ_ERR_INVALID_ARGUMENT,
+                        "layer %d: hidden size %d differs from layer 0's %d", l, L.gate->cols,
+                        layers[0].gate->cols);
+        if ((st = check_decode_sizes(*L.gate, *L.down, n_tokens, top_k)) != VQ_OK)
+            return fail(st, "layer %d: %s", l, vq_last_error());
+        if (n_tokens > 0 && (!L.topk_ids || !L.topk_weights))
+            return fail(VQ_ERR_INVALID_ARGUMENT, "layer %d: topk_ids and topk_weights must be non-NULL",
+                        l);
     }
-    e = launch_down(dn, n_tokens, top_k, h, topk_ids, z, s);
-    if (e != hipSuccess)
-        return hip_fail(e, "vq_moe_ffn (down)");
-    e = vq::launch_combine(z, topk_weights, n_tokens, top_k, down->rows, y, s);
-    return e == hipSuccess ? ok() : hip_fail(e, "vq_moe_ffn (combine)");
+    return VQ_OK;
+}
+
+VQ_EXPORT size_t vq_moe_stack_workspace_size(const vq_moe_layer *layers, int32_t n_layers,
+                                             int32_t n_tokens, int32_t top_k)
+{
+    if (check_stack(layers, n_layers, n_tokens, top_k) != VQ_OK)
+        return 0;
+    size_t need = 256;
+    for (int32_t l = 0; l < n_layers; ++l)
+        need = std::max(need, decode_ws(*layers[l].gate, *layers[l].down, n_tokens, top_k).total);
+    return need;
+}
+
+VQ_EXPORT vq_status vq_moe_stack(const vq_moe_layer *layers, int32_t n_layers, int32_t n_tokens,
+                                 int32_t top_k, float *hidden, void *workspace,
+                                 size_t workspace_bytes, void *stream)
+{
+    vq_status st = check_stack(layers, n_layers, n_tokens, top_k);
+    if (st != VQ_OK)
+        return st;
+    if (n_tokens == 0 || n_layers == 0)
+        return ok();
+    if (!hidden || !aligned(hidden, 16))
+        return fail(VQ_ERR_INVALID_ARGUMENT,
+                    "hidden: must be a non-NULL, 16-byte aligned device pointer");
+    const size_t need = vq_moe_stack_workspace_size(layers, n_layers, n_tokens, top_k);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(VQ_ERR_WORKSPACE,
+                    "workspace: need %zu bytes, 256-byte aligned (got %zu bytes at %p)", need,
+                    workspace_bytes, workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int32_t l = 0; l < n_layers; ++l) {
+        const vq_moe_layer &L = layers[l];
+        const vq::TensorDev g = vq::to_dev(*L.gate), u = vq::to_dev(*L.up),
+                            dn = vq::to_dev(*L.down);
+        // hidden is read by gate+up and then updated in place by the combine,
+        // which runs after it on the same stream
+        st = run_decode_ffn(g, u, dn, n_tokens, top_k, hidden, true, L.topk_ids, L.topk_weights,
+                            hidden, true, decode_ws(*L.gate, *L.down, n_tokens, top_k), workspace,
+                            s, "vq_moe_stack");
+        if (st != VQ_OK)
+            return st;
+    }
+    return ok();
 }
 
 VQ_EXPORT vq_status vq_moe_gate_up(const vq_tensor *gate, const vq_tensor *up, int32_t n_tokens,
@@ -539,7 +627,7 @@ VQ_EXPORT vq_status vq_moe_combine(int32_t n_tokens, int32_t top_k, int32_t hidd
     if (!z || !aligned(z, 16) || !y || !aligned(y, 16) || !topk_weights)
         return fail(VQ_ERR_INVALID_ARGUMENT,
                     "z and y (16-byte aligned) and topk_weights must be non-NULL device pointers");
-    hipError_t e = vq::launch_combine(z, topk_weights, n_tokens, top_k, hidden, y,
+    hipError_t e = vq::launch_combine(z, topk_weights, n_tokens, top_k, hidden, y, false,
                                       static_cast<hipStream_t>(stream));
     return e == hipSuccess ? ok() : hip_fail(e, "vq_moe_combine");
 }

@@ -46,7 +46,7 @@ VQ_DECL_D(8)
 // --------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ z,
                                                  const float *__restrict__ w, int n_tok, int top_k,
-                                                 int hidden, float *__restrict__ y)
+                                                 int hidden, float *__restrict__ y, int accumulate)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t n4 = (int64_t)n_tok * hidden / 4;
@@ -65,18 +65,24 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ z,
         acc.z += ws * v.z;
         acc.w += ws * v.w;
     }
-    *reinterpret_cast<float4 *>(y + t * hidden + c) = acc;
+    float4 *yp = reinterpret_cast<float4 *>(y + t * hidden + c);
+    if (accumulate) {
+        const float4 old = *yp;
+        acc = make_float4(old.x + acc.x, old.y + acc.y, old.z + acc.z, old.w + acc.w);
+    }
+    *yp = acc;
 }
 
 
 hipError_t launch_combine(const float *z, const float *w, int n_tok, int top_k, int hidden,
-                          float *y, hipStream_t stream)
+                          float *y, bool accumulate, hipStream_t stream)
 {
     const int64_t n4 = (int64_t)n_tok * hidden / 4;
     if (n4 == 0)
         return hipSuccess;
     const int blocks = (int)((n4 + 255) / 256);
-    hipLaunchKernelGGL(k_combine, dim3(blocks), dim3(256), 0, stream, z, w, n_tok, top_k, hidden, y);
+    hipLaunchKernelGGL(k_combine, dim3(blocks), dim3(256), 0, stream, z, w, n_tok, top_k, hidden, y,
+                       accumulate ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -190,7 +196,7 @@ hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream)
 
 // The fused down projection and combine: everything but the LDS layout.
 static void mix_args(const TensorDev &dn, int n_tok, int top_k, const float *h, const int32_t *ids,
-                     const float *w, float *y, MixArgs &a)
+                     const float *w, float *y, bool accumulate, MixArgs &a)
 {
     int s_log2 = 0;
     while ((1 << s_log2) < dn.groups)
@@ -210,6 +216,7 @@ static void mix_args(const TensorDev &dn, int n_tok, int top_k, const float *h, 
     a.n_tok = n_tok;
     a.top_k = top_k;
     a.y = y;
+    a.accumulate = accumulate ? 1 : 0;
     const int rpw = 64 >> s_log2;
     a.units = (dn.rows + rpw - 1) / rpw;
     a.max_wgs = 2 * cu_count();
@@ -242,17 +249,18 @@ bool mix_supported(const TensorDev &dn, int n_tok, int top_k)
 }
 
 hipError_t launch_mix(const TensorDev &dn, int n_tok, int top_k, const float *h,
-                      const int32_t *ids, const float *w, float *y, hipStream_t stream)
+                      const int32_t *ids, const float *w, float *y, bool accumulate,
+                      hipStream_t stream)
 {
     if (n_tok == 0 || dn.rows == 0)
         return hipSuccess;
-    if (dn.n_stored == 0)
-        return launch_fill_rows(y, n_tok, dn.rows, dn.rows, stream);
+    if (dn.n_stored == 0)   // every row dead: the sum is +0.0
+        return accumulate ? hipSuccess : launch_fill_rows(y, n_tok, dn.rows, dn.rows, stream);
     MixArgs a = {};
     const int end = mix_layout(dn, n_tok, top_k, (dn.cb_dwords + 3) & ~3, a);
     if (end == 0)
         return hipErrorInvalidValue;
-    mix_args(dn, n_tok, top_k, h, ids, w, y, a);
+    mix_args(dn, n_tok, top_k, h, ids, w, y, accumulate, a);
     const size_t lds = (size_t)end * 4;
     switch (dn.d) {
     case 2: return mix_d<2>(dn.bits, a, lds, stream);

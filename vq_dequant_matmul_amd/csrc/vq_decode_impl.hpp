@@ -754,6 +754,7 @@ struct MixArgs {
     const float *w;          // [P]
     int n_tok, top_k;
     float *y;                // [n_tok][rows]
+    int accumulate;          // 1: y += the combined sum (a residual stream)
     int list_offset, x_offset, m_offset, y_offset;   // LDS dword offsets
     int units;               // tiles of rpw rows
     int max_wgs;             // grid cap (a few workgroups per CU)
@@ -1013,8 +1014,10 @@ struct MixEngine {
 #pragma unroll
                 for (int w = 0; w < kWaves; ++w)
                     v += yall[w * 64 * a.n_tok + i];
-                if (rr < a.rows)
-                    a.y[(int64_t)t * a.rows + rr] = v;
+                if (rr < a.rows) {
+                    float *yp = a.y + (int64_t)t * a.rows + rr;
+                    *yp = a.accumulate ? *yp + v : v;
+                }
             }
             __syncthreads();
         }

@@ -49,9 +49,10 @@ struct RowsLaunch {
 
 hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream);
 
-// y[t][c] = sum_s w[t][s] * z[t*k + s][c], slot order.
+// y[t][c] = sum_s w[t][s] * z[t*k + s][c], slot order (accumulate: y[t][c] +=
+// that sum).
 hipError_t launch_combine(const float *z, const float *w, int n_tok, int top_k, int hidden,
-                          float *y, hipStream_t stream);
+                          float *y, bool accumulate, hipStream_t stream);
 
 hipError_t launch_dequantize(const TensorDev &t, int expert, float *w, hipStream_t stream);
 
@@ -60,11 +61,12 @@ hipError_t launch_gather(const TensorDev &t, int64_t n, const int64_t *ids, floa
                          hipStream_t stream);
 
 // Down projection fused with the slot-ordered combine for a few tokens:
-// y[t] = sum_s w[t][s] * W_down_{e[t][s]} h[t*top_k + s].  mix_supported()
-// tells whether the shapes fit the fused kernel.
+// y[t] = sum_s w[t][s] * W_down_{e[t][s]} h[t*top_k + s] (accumulate: y[t] +=
+// that sum).  mix_supported() tells whether the shapes fit the fused kernel.
 bool mix_supported(const TensorDev &dn, int n_tok, int top_k);
 hipError_t launch_mix(const TensorDev &dn, int n_tok, int top_k, const float *h,
-                      const int32_t *ids, const float *w, float *y, hipStream_t stream);
+                      const int32_t *ids, const float *w, float *y, bool accumulate,
+                      hipStream_t stream);
 
 // Prefill (MFMA) path.
 struct GemmLaunch;

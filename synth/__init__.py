@@ -314,12 +314,12 @@ def make_gather_ids(wl: GatherWorkload, step: int = 0) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# Stacks of MoE layers with promoted layers.  "GLM-5.3-Flash-VQ-2.7bpw" keeps
-# its experts at d=4/K=512 and promotes layers 20, 27, 29, 31, 33, 34, 35 and
-# 39 to d=4/K=2048; "Qwen3.8-Flash-Next-VQ-4.4bpw" keeps d=2/K=256 and
-# promotes layers 0, 1, 2, 16, 24, 31 and 39 to d=2/K=1024 (both opening
-# summaries).  40 layers as on those cards; the layer shapes are the decode
-# workloads' above.  A layer adds its FFN output to the running state, and an
+# Stacks of MoE layers with promoted layers.  "GLM-5.3-Flash-VQ-2.7bpw" fits
+# its 42 expert layers (L3-L44, "Methodology") at d=4/K=512 and promotes
+# layers 20, 27, 29, 31, 33, 34, 35 and 39 to d=4/K=2048;
+# "Qwen3.8-Flash-Next-VQ-4.4bpw" keeps d=2/K=256 and promotes layers 0, 1, 2,
+# 16, 24, 31 and 39 (of 40) to d=2/K=1024 (both opening summaries).  The
+# layer shapes are the decode workloads' above.  A layer adds its FFN output to the running state, and an
 # FFN of random weights grows about quadratically with its input, so forty
 # of them at the experts' usual scales overflow fp32.  In the stacks the down
 # projections' scales are drawn 64 times smaller (U(0.01, 0.05) / 64), which
@@ -334,12 +334,14 @@ STACK_DOWN_SCALES = (0.01 / 64, 0.05 / 64)
 class StackWorkload:
     name: str
     n_layers: int
-    promoted: tuple
+    promoted: tuple            # model layer numbers
     base: MoEWorkload          # shapes, routing and the base geometry
     promoted_bits: int         # same d, wider code
+    first_layer: int = 0       # model layer number of stack position 0
 
     def layer_bits(self, layer: int) -> int:
-        return self.promoted_bits if layer in self.promoted else self.base.bits
+        """Code width at stack position `layer`."""
+        return self.promoted_bits if layer + self.first_layer in self.promoted else self.base.bits
 
     def layer_workload(self, layer: int) -> MoEWorkload:
         b = self.base
@@ -349,9 +351,9 @@ class StackWorkload:
 
 
 STACK_WORKLOADS = {
-    "moe_stack40_e128_h2048_i768_d4k512_p8k2048_b1": StackWorkload(
-        "moe_stack40_e128_h2048_i768_d4k512_p8k2048_b1", 40, (20, 27, 29, 31, 33, 34, 35, 39),
-        WORKLOADS["moe_decode_e128_h2048_i768_d4k512_b1"], 11),
+    "moe_stack42_e128_h2048_i768_d4k512_p8k2048_b1": StackWorkload(
+        "moe_stack42_e128_h2048_i768_d4k512_p8k2048_b1", 42, (20, 27, 29, 31, 33, 34, 35, 39),
+        WORKLOADS["moe_decode_e128_h2048_i768_d4k512_b1"], 11, first_layer=3),
     "moe_stack40_e512_h4096_i1024_d2k256_p7k1024_b1": StackWorkload(
         "moe_stack40_e512_h4096_i1024_d2k256_p7k1024_b1", 40, (0, 1, 2, 16, 24, 31, 39),
         WORKLOADS["moe_decode_e512_h4096_i1024_d2k256_b1"], 10),

@@ -142,10 +142,10 @@ def test_stack_errors():
         vq.vq_moe_stack(dev[:1], torch.zeros((17, 256), device="cuda"))
 
 
-@pytest.mark.parametrize("name", ["moe_stack40_e128_h2048_i768_d4k512_p8k2048_b1"])
+@pytest.mark.parametrize("name", ["moe_stack42_e128_h2048_i768_d4k512_p8k2048_b1"])
 def test_full_size_stack(name):
-    """The 40-layer stack of the measured workload (one token, eight
-    promoted 11-bit layers), every layer against the oracle."""
+    """The 42-layer stack of the measured workload (one token, eight
+    promoted 11-bit layers), against the oracle."""
     sw = synth.STACK_WORKLOADS[name]
     host = {}
     for l in range(sw.n_layers):

@@ -13,6 +13,9 @@ decode W = scale * codebook[code] exactly in fp32, multiply with fp64
 accumulation, and for the MoE FFN apply SwiGLU and the gate-weighted sum over
 the routed experts in fp64.  ``gather`` reads single decoded rows, as the
 per-layer n-gram embedding tables of "Qwen3.8-Flash-Next-VQ-4.4bpw" are read.
+``fit`` (with ``fit_scales``, ``kmeans``, ``encode``) produces the format from
+bf16 weights by k-means / Lloyd over the weight subvectors (the cards'
+"Methodology" sections).
 
 Tensor arguments are any object with the attributes ``rows, cols, d, bits, K,
 n_experts, codebook (uint16 [K, d]), codes (uint32 [n_stored, wpr]), scales
@@ -39,7 +42,7 @@ def build(force: bool = True) -> str:
     """Compile the oracle with gcc (OpenMP over independent output rows)."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+        cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-fopenmp",
                "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
@@ -90,6 +93,17 @@ def _load():
         lib.vqo_moe_stack.restype = ctypes.c_int
         lib.vqo_moe_stack.argtypes = [ctypes.c_int32, P, P, P, ctypes.c_int32, ctypes.c_int32,
                                       P, P, P]
+        I64, I32 = ctypes.c_int64, ctypes.c_int32
+        lib.vqo_float_to_half.restype = ctypes.c_uint16
+        lib.vqo_float_to_half.argtypes = [ctypes.c_float]
+        lib.vqo_fit_scales.restype = ctypes.c_int
+        lib.vqo_fit_scales.argtypes = [I64, I32, P, P]
+        lib.vqo_kmeans.restype = ctypes.c_int
+        lib.vqo_kmeans.argtypes = [I64, I32, I32, I32, P, P, I64, P, P, I32, P]
+        lib.vqo_encode.restype = ctypes.c_int
+        lib.vqo_encode.argtypes = [I64, I32, I32, I32, I32, P, P, P, P]
+        lib.vqo_fit.restype = ctypes.c_int
+        lib.vqo_fit.argtypes = [I64, I32, I32, I32, I32, P, I64, P, P, I32, P, P, P]
         lib.vqo_swiglu.restype = ctypes.c_double
         lib.vqo_swiglu.argtypes = [ctypes.c_double, ctypes.c_double]
         _lib = lib
@@ -232,6 +246,66 @@ def moe_stack(layers, x: np.ndarray) -> np.ndarray:
                                _ptr(h))
     _raise(rc, "moe_stack")
     return h
+
+
+# ---- fitting the format -------------------------------------------------
+
+def float_to_half(f: float) -> int:
+    """fp16 bits of an fp32 value, round to nearest even."""
+    return int(_load().vqo_float_to_half(f))
+
+
+def fit_scales(w: np.ndarray) -> np.ndarray:
+    """fp16 bits [n_rows, cols/64]: max |w| per group, w bf16 bits [n_rows, cols]."""
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    sc = np.zeros((w.shape[0], w.shape[1] // 64), dtype=np.uint16)
+    _raise(_load().vqo_fit_scales(w.shape[0], w.shape[1], _ptr(w), _ptr(sc)), "fit_scales")
+    return sc
+
+
+def kmeans(w: np.ndarray, scales: np.ndarray, d: int, K: int, sample, init,
+           iters: int) -> np.ndarray:
+    """fp32 centroids [K, d] after `iters` Lloyd iterations on the normalised
+    subvectors named by `sample`, from those named by `init`."""
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    sample = np.ascontiguousarray(sample, dtype=np.int64)
+    init = np.ascontiguousarray(init, dtype=np.int64)
+    C = np.zeros((K, d), dtype=np.float32)
+    rc = _load().vqo_kmeans(w.shape[0], w.shape[1], d, K, _ptr(w), _ptr(scales), len(sample),
+                            _ptr(sample) if len(sample) else None, _ptr(init), iters, _ptr(C))
+    _raise(rc, "kmeans")
+    return C
+
+
+def encode(w: np.ndarray, scales: np.ndarray, codebook: np.ndarray, d: int,
+           bits: int) -> np.ndarray:
+    """Packed codes [n_rows, wpr]: every subvector's nearest fp16 entry."""
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    cb = np.ascontiguousarray(codebook, dtype=np.uint16)
+    codes = np.zeros((w.shape[0], words_per_row(w.shape[1], d, bits)), dtype=np.uint32)
+    rc = _load().vqo_encode(w.shape[0], w.shape[1], d, bits, cb.shape[0], _ptr(w), _ptr(scales),
+                            _ptr(cb), _ptr(codes))
+    _raise(rc, "encode")
+    return codes
+
+
+def fit(w: np.ndarray, d: int, bits: int, K: int, sample, init, iters: int):
+    """The whole fit: (codebook fp16 bits [K, d], scales fp16 bits
+    [n_rows, cols/64], packed codes [n_rows, wpr])."""
+    w = np.ascontiguousarray(w, dtype=np.uint16)
+    sample = np.ascontiguousarray(sample, dtype=np.int64)
+    init = np.ascontiguousarray(init, dtype=np.int64)
+    n_rows, cols = w.shape
+    cb = np.zeros((K, d), dtype=np.uint16)
+    sc = np.zeros((n_rows, cols // 64), dtype=np.uint16)
+    codes = np.zeros((n_rows, words_per_row(cols, d, bits)), dtype=np.uint32)
+    rc = _load().vqo_fit(n_rows, cols, d, bits, K, _ptr(w), len(sample),
+                         _ptr(sample) if len(sample) else None, _ptr(init), iters, _ptr(cb),
+                         _ptr(sc), _ptr(codes))
+    _raise(rc, "fit")
+    return cb, sc, codes
 
 
 def swiglu(g: float, u: float) -> float:

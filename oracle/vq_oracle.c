@@ -439,3 +439,226 @@ int vqo_moe_stack(int32_t n_layers, const vqo_tensor *const *gate,
     free(y);
     return err;
 }
+
+/* ---------------------------------------------------------------------- */
+/* Step 0: fitting the format (the step before the path)                   */
+/* ---------------------------------------------------------------------- */
+
+/* The cards fit codebooks "data-free" by k-means / Lloyd over the weight
+   subvectors, from a subsample drawn unseeded or with seed 1234, with an
+   fp16 scale per (row, 64 weights) and the codes packed sub-byte
+   ("Qwen3.5-397B-A17B-VQ-2.6bpw", "Methodology"; "Qwen3.5-397B-A17B-VQ-2.4bpw:
+   Model Card", "Methodology"; "Qwen3.8-Flash-Next-VQ-4.4bpw" and
+   "GLM-5.3-Flash-VQ-2.7bpw", "Methodology").  They do not say how a
+   scale is chosen, how the fit is initialised or how many iterations run.
+   The readings taken here:
+     - scale s[r][g] = fp16 (round to nearest even) of max |w| over the
+       group; a subvector is normalised as v_t = w_t / s in fp32 (IEEE
+       division), and a group with s == 0 normalises to zeros;
+     - the fit runs on a given set of subvector indices (the subsample) from
+       K given initial subvectors (the seeded draw is an input) for a given
+       number of Lloyd iterations;
+     - distance = sum over t, in order, of (v_t - c_t)^2 in fp32 with every
+       operation rounded (no fused multiply-add); ties go to the lower index;
+     - a centroid is the mean of its members, summed exactly as integers in
+       units of 2^-30 (each coordinate rounded to nearest even into that
+       grid) and divided in fp64; a centroid with no members keeps its value;
+     - the codebook is the centroids rounded to fp16, and every subvector of
+       the tensor is then coded to its nearest fp16 entry (same distance).
+   With these, a result is a function of its inputs alone, independent of
+   the order in which members are visited. */
+
+/* Built with -ffp-contract=off: every fp32 operation below rounds on its own. */
+
+/* fp32 -> fp16 bits, round to nearest, ties to even (IEEE 754 conversion):
+   scale |f| onto the 11-bit significand grid of its binade (the subnormal
+   grid below 2^-14) in fp64, where the scaling is exact, and round there. */
+uint16_t vqo_float_to_half(float f)
+{
+    if (isnan(f))
+        return 0x7e00;
+    const uint16_t sign = signbit(f) ? 0x8000 : 0;
+    const double a = fabs((double)f);
+    if (a >= 65520.0)            /* at or above the midpoint past 65504 */
+        return sign | 0x7c00;
+    int e;
+    frexp(a, &e);                /* a in [2^(e-1), 2^e) */
+    int ex = e - 1;
+    if (ex < -14)
+        ex = -14;                /* subnormal grid: 2^-24 */
+    double q = nearbyint(ldexp(a, 10 - ex));
+    if (q >= 2048.0) {           /* rounded up into the next binade */
+        ex += 1;
+        q = 1024.0;
+    }
+    if (q < 1024.0)              /* subnormal or zero */
+        return sign | (uint16_t)q;
+    return sign | (uint16_t)(((ex + 15) << 10) | ((int)q - 1024));
+}
+
+static float bf16_to_float(uint16_t h)
+{
+    return (float)vqo_bf16_to_double(h);   /* exact: bf16 is a prefix of fp32 */
+}
+
+int vqo_fit_scales(int64_t n_rows, int32_t cols, const uint16_t *w, uint16_t *scales)
+{
+    if (n_rows < 0 || cols <= 0 || cols % 64 || (n_rows > 0 && (!w || !scales)))
+        return VQO_EBADARG;
+    const int32_t groups = cols / 64;
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int32_t g = 0; g < groups; ++g) {
+            float m = 0.0f;
+            for (int32_t c = 0; c < 64; ++c) {
+                float a = fabsf(bf16_to_float(w[r * cols + 64 * g + c]));
+                if (a > m)
+                    m = a;
+            }
+            scales[r * groups + g] = vqo_float_to_half(m);
+        }
+    return VQO_OK;
+}
+
+/* Normalised subvector i = r*(cols/d) + j of the tensor. */
+static void subvector(const uint16_t *w, const uint16_t *scales, int32_t cols, int32_t d,
+                      int64_t i, float *v)
+{
+    const int64_t n_sub = cols / d;
+    const int64_t r = i / n_sub, j = i % n_sub;
+    const float s = (float)vqo_half_to_double(scales[r * (cols / 64) + (j * d) / 64]);
+    for (int32_t t = 0; t < d; ++t)
+        v[t] = (s == 0.0f) ? 0.0f : bf16_to_float(w[r * cols + j * d + t]) / s;
+}
+
+static float dist2(const float *x, const float *c, int32_t d)
+{
+    float acc = 0.0f;
+    for (int32_t t = 0; t < d; ++t) {
+        const float diff = x[t] - c[t];
+        const float sq = diff * diff;
+        acc = acc + sq;
+    }
+    return acc;
+}
+
+static int32_t nearest(const float *x, const float *C, int32_t K, int32_t d)
+{
+    int32_t best = 0;
+    float bd = dist2(x, C, d);
+    for (int32_t k = 1; k < K; ++k) {
+        const float dk = dist2(x, C + (int64_t)k * d, d);
+        if (dk < bd) {
+            bd = dk;
+            best = k;
+        }
+    }
+    return best;
+}
+
+#define VQO_FIT_MAX_SAMPLE (1 << 22)   /* keeps every integer sum below 2^53 */
+
+int vqo_kmeans(int64_t n_rows, int32_t cols, int32_t d, int32_t K, const uint16_t *w,
+               const uint16_t *scales, int64_t n_sample, const int64_t *sample,
+               const int64_t *init, int32_t iters, float *C)
+{
+    const int64_t N = n_rows * (cols / (d > 0 ? d : 1));
+    if (n_rows < 1 || cols <= 0 || cols % 64 || (d != 2 && d != 4 && d != 8) || K < 1 ||
+        n_sample < 0 || n_sample > VQO_FIT_MAX_SAMPLE || iters < 0 || !w || !scales || !init ||
+        !C || (n_sample > 0 && !sample))
+        return VQO_EBADARG;
+    for (int32_t k = 0; k < K; ++k)
+        if (init[k] < 0 || init[k] >= N)
+            return VQO_EBADARG;
+    for (int64_t i = 0; i < n_sample; ++i)
+        if (sample[i] < 0 || sample[i] >= N)
+            return VQO_EBADARG;
+    for (int32_t k = 0; k < K; ++k)
+        subvector(w, scales, cols, d, init[k], C + (int64_t)k * d);
+
+    int64_t *sum = (int64_t *)calloc((size_t)K * d + 1, sizeof(int64_t));
+    int64_t *cnt = (int64_t *)calloc((size_t)K + 1, sizeof(int64_t));
+    if (!sum || !cnt) {
+        free(sum);
+        free(cnt);
+        return VQO_ENOMEM;
+    }
+    float v[8];
+    for (int32_t it = 0; it < iters; ++it) {
+        memset(sum, 0, sizeof(int64_t) * (size_t)K * d);
+        memset(cnt, 0, sizeof(int64_t) * (size_t)K);
+        for (int64_t i = 0; i < n_sample; ++i) {
+            subvector(w, scales, cols, d, sample[i], v);
+            const int32_t k = nearest(v, C, K, d);
+            cnt[k] += 1;
+            for (int32_t t = 0; t < d; ++t)
+                sum[(int64_t)k * d + t] += llrint(ldexp((double)v[t], 30));
+        }
+        for (int32_t k = 0; k < K; ++k) {
+            if (cnt[k] == 0)
+                continue;
+            for (int32_t t = 0; t < d; ++t)
+                C[(int64_t)k * d + t] =
+                    (float)ldexp((double)sum[(int64_t)k * d + t] / (double)cnt[k], -30);
+        }
+    }
+    free(sum);
+    free(cnt);
+    return VQO_OK;
+}
+
+int vqo_encode(int64_t n_rows, int32_t cols, int32_t d, int32_t bits, int32_t K,
+               const uint16_t *w, const uint16_t *scales, const uint16_t *codebook,
+               uint32_t *codes)
+{
+    if (n_rows < 0 || cols <= 0 || cols % 64 || (d != 2 && d != 4 && d != 8) || K < 1 ||
+        bits < 1 || bits > 16 || (int64_t)K > ((int64_t)1 << bits) ||
+        (n_rows > 0 && (!w || !scales || !codebook || !codes)))
+        return VQO_EBADARG;
+    float *C = (float *)malloc(sizeof(float) * (size_t)K * d);
+    if (!C)
+        return VQO_ENOMEM;
+    for (int64_t i = 0; i < (int64_t)K * d; ++i)
+        C[i] = (float)vqo_half_to_double(codebook[i]);
+    const int64_t n_sub = cols / d, wpr = vqo_words_per_row(cols, d, bits);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        uint32_t *row = codes + r * wpr;
+        float v[8];
+        for (int64_t q = 0; q < wpr; ++q)
+            row[q] = 0;
+        /* code j occupies stream bits [j*bits, j*bits + bits), LSB first */
+        for (int64_t j = 0; j < n_sub; ++j) {
+            subvector(w, scales, cols, d, r * n_sub + j, v);
+            const uint32_t code = (uint32_t)nearest(v, C, K, d);
+            for (int32_t b = 0; b < bits; ++b)
+                if ((code >> b) & 1u) {
+                    const int64_t q = j * bits + b;
+                    row[q / 32] |= 1u << (q % 32);
+                }
+        }
+    }
+    free(C);
+    return VQO_OK;
+}
+
+int vqo_fit(int64_t n_rows, int32_t cols, int32_t d, int32_t bits, int32_t K, const uint16_t *w,
+            int64_t n_sample, const int64_t *sample, const int64_t *init, int32_t iters,
+            uint16_t *codebook, uint16_t *scales, uint32_t *codes)
+{
+    if (!codebook || (int64_t)K > ((int64_t)1 << (bits > 0 && bits < 31 ? bits : 0)))
+        return VQO_EBADARG;
+    int err = vqo_fit_scales(n_rows, cols, w, scales);
+    if (err != VQO_OK)
+        return err;
+    float *C = (float *)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1) * 8);
+    if (!C)
+        return VQO_ENOMEM;
+    err = vqo_kmeans(n_rows, cols, d, K, w, scales, n_sample, sample, init, iters, C);
+    if (err == VQO_OK) {
+        for (int64_t i = 0; i < (int64_t)K * d; ++i)
+            codebook[i] = vqo_float_to_half(C[i]);
+        err = vqo_encode(n_rows, cols, d, bits, K, w, scales, codebook, codes);
+    }
+    free(C);
+    return err;
+}

@@ -112,6 +112,32 @@ int vqo_moe_stack(int32_t n_layers, const vqo_tensor *const *gate,
                   int32_t n_tok, int32_t top_k, const int32_t *const *ids,
                   const float *const *w, double *h);
 
+/* ---- Step 0: fitting the format (test infrastructure for the fit) ---- */
+
+/* fp32 -> fp16 bits, round to nearest even. */
+uint16_t vqo_float_to_half(float f);
+
+/* scales[r][g] = fp16(max |w[r][64g .. 64g+63]|); w: bf16 bits [n_rows][cols]. */
+int vqo_fit_scales(int64_t n_rows, int32_t cols, const uint16_t *w, uint16_t *scales);
+
+/* Lloyd's k-means on the normalised subvectors named by sample[0..n_sample)
+   (subvector i = r*(cols/d) + j), from the K subvectors named by init, for
+   iters iterations; C: fp32 [K][d] out.  n_sample <= 2^22. */
+int vqo_kmeans(int64_t n_rows, int32_t cols, int32_t d, int32_t K, const uint16_t *w,
+               const uint16_t *scales, int64_t n_sample, const int64_t *sample,
+               const int64_t *init, int32_t iters, float *C);
+
+/* Every subvector coded to its nearest fp16 codebook entry and packed:
+   codes [n_rows][words_per_row]. */
+int vqo_encode(int64_t n_rows, int32_t cols, int32_t d, int32_t bits, int32_t K,
+               const uint16_t *w, const uint16_t *scales, const uint16_t *codebook,
+               uint32_t *codes);
+
+/* scales, k-means, fp16 codebook, encode: the whole fit. */
+int vqo_fit(int64_t n_rows, int32_t cols, int32_t d, int32_t bits, int32_t K, const uint16_t *w,
+            int64_t n_sample, const int64_t *sample, const int64_t *init, int32_t iters,
+            uint16_t *codebook, uint16_t *scales, uint32_t *codes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -217,6 +217,38 @@ vq_status vq_moe_stack(const vq_moe_layer *layers, int32_t n_layers, int32_t n_t
                        int32_t top_k, float *hidden, void *workspace, size_t workspace_bytes,
                        void *stream);
 
+/* ---- fitting the format ------------------------------------------------------- */
+
+/* The step before the path: produce codebook, scales and packed codes from
+   bf16 weights.  The cards fit "data-free" by k-means / Lloyd over the
+   weight subvectors from a seeded or unseeded subsample, with an fp16 scale
+   per (row, 64 weights) ("Methodology" sections of the Qwen3.5-397B-A17B
+   2.6bpw and 2.4bpw, Qwen3.8-Flash-Next and GLM-5.3-Flash cards).  Here:
+     scales[r][g] = fp16 (nearest even) of max |w| over the group;
+     subvector i = r*(cols/d) + j is v = w[r][j*d .. j*d+d) / s in fp32
+       (a group with s == 0 gives zeros);
+     centroids start at the subvectors init[0..K); each of `iters` Lloyd
+       passes assigns every subvector named in sample[0..n_sample) to its
+       nearest centroid and moves each centroid with members to their mean
+       (distances: fp32 sums of rounded squares in coordinate order, ties to
+       the lower index; means: exact integer sums on a 2^-30 grid divided
+       in fp64), so the result does not depend on thread order;
+     codebook = the centroids in fp16; every subvector of the tensor is
+       coded to its nearest codebook entry and packed as in the layout above.
+   The outputs form a dense vq_tensor with rows = n_rows (no row map).
+   w: device bf16 [n_rows][cols], 16-byte aligned; sample, init: device
+   int64 subvector indices (in range: a precondition; out-of-range values
+   are clamped), n_sample <= 2^22; codebook: device fp16 [K][d]; scales:
+   device fp16 [n_rows][cols/64]; codes: device uint32 [n_rows][wpr].
+   K*d <= 16384 (the centroids are searched from LDS as fp32).  Weights must
+   be finite with |w| <= 65504.  workspace: at least vq_fit_workspace_size()
+   bytes, 256-byte aligned. */
+size_t vq_fit_workspace_size(int32_t d, int32_t K, int64_t n_sample);
+vq_status vq_fit(int64_t n_rows, int32_t cols, int32_t d, int32_t bits, int32_t K,
+                 const uint16_t *w, int64_t n_sample, const int64_t *sample,
+                 const int64_t *init, int32_t iters, uint16_t *codebook, uint16_t *scales,
+                 uint32_t *codes, void *workspace, size_t workspace_bytes, void *stream);
+
 /* ---- measurement -------------------------------------------------------------- */
 
 /* Until cleared (NULL, NULL), every vq_moe_ffn / vq_moe_gate_up /

@@ -378,3 +378,17 @@ def make_stack_layer(sw: StackWorkload, layer: int):
     """gate, up, down of stack layer `layer` (layers of one geometry share
     their values)."""
     return make_moe_layer(sw.layer_workload(layer), down_scale_range=STACK_DOWN_SCALES)
+
+
+# --------------------------------------------------------------------------
+# Weights to fit the format to.  The cards fit real bf16 checkpoints; these
+# stand in for them: N(0, 0.02) with 2 % of the weights four times larger
+# (a heavier tail, as trained weights have), rounded to bf16.
+# --------------------------------------------------------------------------
+
+def make_fit_weights(seed: int, n_rows: int, cols: int) -> np.ndarray:
+    """bf16 bit patterns [n_rows, cols]."""
+    g = rng_for(seed, 60_000)
+    w = g.standard_normal((n_rows, cols)).astype(np.float32) * np.float32(0.02)
+    w *= np.where(g.random((n_rows, cols)) < 0.02, np.float32(4.0), np.float32(1.0))
+    return to_bf16_bits(w)

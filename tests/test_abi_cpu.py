@@ -143,3 +143,25 @@ def test_row_gather_argument_errors(lib):
     assert st == 2 and "d = 3" in lib.vq_last_error().decode()
     # zero rows is a no-op, whatever the pointers
     assert lib.vq_row_gather(ctypes.byref(t), 0, None, None, None) == 0
+
+
+def test_fit_argument_errors(lib):
+    assert lib.vq_fit_workspace_size(4, 512, 1000) >= 1000 * 16 + 512 * 16
+    ws = lib.vq_fit_workspace_size(4, 512, 100)
+    def call(**kw):
+        a = dict(n_rows=8, cols=128, d=4, bits=9, K=512, w=FAKE, n_sample=100, sample=FAKE,
+                 init=FAKE, iters=2, cb=FAKE, sc=FAKE, codes=FAKE, ws=FAKE, wsb=ws)
+        a.update(kw)
+        return lib.vq_fit(a["n_rows"], a["cols"], a["d"], a["bits"], a["K"], a["w"],
+                          a["n_sample"], a["sample"], a["init"], a["iters"], a["cb"], a["sc"],
+                          a["codes"], a["ws"], a["wsb"], None)
+    for kw, status, needle in [
+        (dict(n_rows=0), 1, "n_rows"), (dict(cols=100), 1, "cols"), (dict(d=3), 2, "d = 3"),
+        (dict(bits=14), 2, "bits"), (dict(K=513), 1, "K = 513"),
+        (dict(d=8, bits=13, K=4096), 2, "K*d"), (dict(n_sample=(1 << 22) + 1), 1, "n_sample"),
+        (dict(iters=-1), 1, "iters"), (dict(w=FAKE + 8), 1, "w:"), (dict(init=None), 1, "init"),
+        (dict(codes=FAKE + 2), 1, "codes"), (dict(wsb=ws - 1), 3, "workspace"),
+    ]:
+        st = call(**kw)
+        assert st == status, (kw, st)
+        assert needle in lib.vq_last_error().decode(), (kw, lib.vq_last_error())

@@ -76,6 +76,8 @@ def load_library():
         "vq_validate": (ctypes.c_int, [T]),
         "vq_dequantize": (ctypes.c_int, [T, I32, P, P]),
         "vq_row_gather": (ctypes.c_int, [T, I64, P, P, P]),
+        "vq_fit_workspace_size": (SZ, [I32, I32, I64]),
+        "vq_fit": (ctypes.c_int, [I64, I32, I32, I32, I32, P, I64, P, P, I32, P, P, P, P, SZ, P]),
         "vq_expert_gemv": (ctypes.c_int, [T, I32, I32, P, ctypes.c_int, P, P]),
         "vq_expert_gemm_workspace_size": (SZ, [T, I32]),
         "vq_expert_gemm": (ctypes.c_int, [T, I32, P, ctypes.c_int, P, P, P, SZ, P]),
@@ -225,6 +227,33 @@ def vq_row_gather(W: VQTensor, ids: torch.Tensor,
     c = W.c()
     _check(lib.vq_row_gather(ctypes.byref(c), n, _ptr(ids), _ptr(out), _stream()))
     return out
+
+
+def vq_fit(w: torch.Tensor, d: int, bits: int, K: int, sample: torch.Tensor,
+           init: torch.Tensor, iters: int, workspace: Optional[torch.Tensor] = None):
+    """Fit the format to bf16 weights w [n_rows, cols]: returns (codebook
+    int16 [K, d] fp16 bits, scales int16 [n_rows, cols/64] fp16 bits, codes
+    int32 [n_rows, wpr]), a dense tensor's arrays (see vq.h, vq_fit)."""
+    _require_gpu()
+    lib = load_library()
+    if w.dtype != torch.bfloat16 or w.dim() != 2 or not w.is_contiguous():
+        raise TypeError("w must be a contiguous 2-D bfloat16 device tensor")
+    for name, t in (("sample", sample), ("init", init)):
+        if t.dtype != torch.int64 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous int64 device tensor")
+    n_rows, cols = w.shape
+    wpr = ((cols // d + 31) // 32) * bits
+    dev = w.device
+    codebook = torch.empty((K, d), dtype=torch.int16, device=dev)
+    scales = torch.empty((n_rows, cols // 64), dtype=torch.int16, device=dev)
+    codes = torch.empty((n_rows, wpr), dtype=torch.int32, device=dev)
+    if workspace is None:
+        ws = lib.vq_fit_workspace_size(d, K, sample.numel())
+        workspace = torch.empty(max(int(ws), 256), dtype=torch.uint8, device=dev)
+    _check(lib.vq_fit(n_rows, cols, d, bits, K, _ptr(w), sample.numel(), _ptr(sample),
+                      _ptr(init), iters, _ptr(codebook), _ptr(scales), _ptr(codes),
+                      _ptr(workspace), workspace.numel(), _stream()))
+    return codebook, scales, codes
 
 
 def vq_expert_gemv(W: VQTensor, expert: int, x: torch.Tensor,
@@ -385,7 +414,7 @@ def vq_set_kernel_events(start, stop) -> None:
 
 __all__ = [
     "VQError", "VQTensor", "build", "load_library", "vq_validate", "vq_dequantize",
-    "vq_row_gather",
+    "vq_row_gather", "vq_fit",
     "vq_expert_gemv", "vq_expert_gemm", "vq_expert_gemm_workspace_size", "vq_moe_ffn",
     "vq_moe_ffn_workspace_size", "vq_moe_gate_up", "vq_moe_down", "vq_moe_combine",
     "vq_set_kernel_events", "vq_moe_stack", "vq_moe_stack_workspace_size",

@@ -16,7 +16,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libvqmm.so")
 SOURCES = ["vq_api.cpp", "vq_decode.hip", "vq_decode_d2.hip", "vq_decode_d4.hip",
            "vq_decode_d8.hip", "vq_prefill.hip", "vq_prefill_d2.hip", "vq_prefill_d4.hip",
-           "vq_prefill_d8.hip", "vq_gather.hip"]
+           "vq_prefill_d8.hip", "vq_gather.hip", "vq_fit.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -211,6 +211,88 @@ VQ_EXPORT vq_status vq_dequantize(const vq_tensor *W, int32_t expert, float *w, 
 }
 
 // ------------------------------------------------------------------------------------
+// fitting the format
+// ------------------------------------------------------------------------------------
+
+constexpr int64_t kFitMaxSample = (int64_t)1 << 22;   // keeps the integer sums below 2^53
+
+static vq_status check_fit(int64_t n_rows, int32_t cols, int32_t d, int32_t bits, int32_t K,
+                           int64_t n_sample, int32_t iters)
+{
+    if (n_rows < 1)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "n_rows = %lld: must be >= 1", (long long)n_rows);
+    if (cols < 64 || cols % 64 != 0)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "cols = %d: must be a positive multiple of 64", cols);
+    if (d != 2 && d != 4 && d != 8)
+        return fail(VQ_ERR_UNSUPPORTED, "d = %d: supported subvector lengths are 2, 4 and 8", d);
+    if (bits < 8 || bits > 13)
+        return fail(VQ_ERR_UNSUPPORTED, "bits = %d: supported code widths are 8..13", bits);
+    if (K < 1 || (int64_t)K > ((int64_t)1 << bits))
+        return fail(VQ_ERR_INVALID_ARGUMENT, "K = %d: need 1 <= K <= 2^bits", K);
+    if ((int64_t)K * d > 16384)
+        return fail(VQ_ERR_UNSUPPORTED,
+                    "K*d = %lld: the fit keeps K*d <= 16384 fp32 centroid values in LDS",
+                    (long long)K * d);
+    if (n_sample < 0 || n_sample > kFitMaxSample)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "n_sample = %lld: must be in [0, %lld]",
+                    (long long)n_sample, (long long)kFitMaxSample);
+    if (iters < 0)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "iters = %d: must be >= 0", iters);
+    if (n_rows > ((int64_t)1 << 40) / cols)
+        return fail(VQ_ERR_UNSUPPORTED, "n_rows = %lld: tensor too large", (long long)n_rows);
+    return VQ_OK;
+}
+
+VQ_EXPORT size_t vq_fit_workspace_size(int32_t d, int32_t K, int64_t n_sample)
+{
+    if (d < 1 || K < 1 || n_sample < 0)
+        return 0;
+    return vq::fit_workspace_bytes(d, K, n_sample, nullptr, nullptr);
+}
+
+VQ_EXPORT vq_status vq_fit(int64_t n_rows, int32_t cols, int32_t d, int32_t bits, int32_t K,
+                           const uint16_t *w, int64_t n_sample, const int64_t *sample,
+                           const int64_t *init, int32_t iters, uint16_t *codebook,
+                           uint16_t *scales, uint32_t *codes, void *workspace,
+                           size_t workspace_bytes, void *stream)
+{
+    vq_status st = check_fit(n_rows, cols, d, bits, K, n_sample, iters);
+    if (st != VQ_OK)
+        return st;
+    if (!w || !aligned(w, 16))
+        return fail(VQ_ERR_INVALID_ARGUMENT, "w: must be a non-NULL, 16-byte aligned device pointer");
+    if (!init || !aligned(init, 8) || (n_sample > 0 && (!sample || !aligned(sample, 8))))
+        return fail(VQ_ERR_INVALID_ARGUMENT,
+                    "init (and sample when n_sample > 0) must be non-NULL, 8-byte aligned");
+    if (!codebook || !scales || !codes || !aligned(codebook, 2) || !aligned(scales, 2) ||
+        !aligned(codes, 4))
+        return fail(VQ_ERR_INVALID_ARGUMENT,
+                    "codebook, scales (2-byte aligned) and codes (4-byte aligned) must be non-NULL");
+    const size_t need = vq::fit_workspace_bytes(d, K, n_sample, nullptr, nullptr);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(VQ_ERR_WORKSPACE,
+                    "workspace: need %zu bytes, 256-byte aligned (got %zu bytes at %p)", need,
+                    workspace_bytes, workspace);
+    vq::FitArgs f;
+    f.n_rows = n_rows;
+    f.cols = cols;
+    f.d = d;
+    f.bits = bits;
+    f.K = K;
+    f.w = w;
+    f.n_sample = n_sample;
+    f.sample = sample;
+    f.init = init;
+    f.iters = iters;
+    f.codebook = codebook;
+    f.scales = scales;
+    f.codes = codes;
+    vq::fit_workspace_bytes(d, K, n_sample, &f, workspace);
+    hipError_t e = vq::launch_fit(f, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "vq_fit");
+}
+
+// ------------------------------------------------------------------------------------
 // row gather
 // ------------------------------------------------------------------------------------
 

@@ -1,0 +1,311 @@
+// vq_fit.hip -- fitting the format: scales, k-means / Lloyd over the weight
+// subvectors, fp16 codebook, encode and pack.
+//
+// The cards fit their codebooks data-free by k-means / Lloyd over the weight
+// subvectors from a seeded or unseeded subsample, with an fp16 scale per
+// (row, 64 weights) and the codes packed sub-byte ("Methodology" sections of
+// the Qwen3.5-397B-A17B 2.6bpw and 2.4bpw, Qwen3.8-Flash-Next and
+// GLM-5.3-Flash cards).  Where they are silent this follows one reading,
+// chosen so that every integer decision (a nearest centroid, a code) is a
+// function of the inputs alone, whatever the thread order:
+//   - scale = fp16 (nearest even) of the group's max |w|; v = w / s in fp32
+//     with IEEE division; a group with s == 0 normalises to zeros;
+//   - the fit set (subsample) and the K initial subvectors are inputs;
+//   - distance = sum over t in order of (v_t - c_t)^2, every fp32 operation
+//     rounded on its own (no fused multiply-add); ties go to the lower index;
+//   - a centroid is the mean of its members: coordinates rounded to nearest
+//     even on a 2^-30 grid and summed as 64-bit integers (integer atomics
+//     are order-independent), the sum divided by the count in fp64; a
+//     centroid without members keeps its value;
+//   - the codebook is the centroids in fp16, and every subvector of the
+//     tensor is coded to its nearest fp16 entry and packed LSB-first into
+//     row-local 32-code blocks.
+// All of it is ALU work on small data: nearest-centroid searches against a
+// codebook held in LDS (K*d fp32 values), K*d subtract-multiply-add triples
+// per subvector.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "vq_common.hpp"
+#include "vq_internal.hpp"
+
+// Every fp32 and fp64 operation in this file rounds on its own (no fused
+// multiply-add forms), as the decisions above require.
+#pragma clang fp contract(off)
+
+namespace vq {
+namespace {
+
+constexpr int kFitThreads = 256;
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ uint16_t float_to_half_bits(float f)
+{
+    const f16 h = (f16)f;   // v_cvt_f16_f32: round to nearest even
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// Distance of x to entry c, every operation rounded: no contraction.
+template <int D>
+__device__ __forceinline__ float dist2(const float (&x)[D], const float *c)
+{
+    float acc = 0.0f;
+#pragma unroll
+    for (int t = 0; t < D; ++t) {
+        const float diff = x[t] - c[t];
+        const float sq = diff * diff;
+        acc = acc + sq;
+    }
+    return acc;
+}
+
+// Index of the nearest of the K entries in LDS (first minimum).
+template <int D>
+__device__ __forceinline__ uint32_t nearest(const float (&x)[D], const float *C, int K)
+{
+    float best = dist2<D>(x, C);
+    uint32_t bk = 0;
+    for (int k = 1; k < K; ++k) {
+        const float dk = dist2<D>(x, C + k * D);
+        if (dk < best) {
+            best = dk;
+            bk = (uint32_t)k;
+        }
+    }
+    return bk;
+}
+
+// Normalised subvector i = r * n_sub + j.
+template <int D>
+__device__ __forceinline__ void subvector(const uint16_t *__restrict__ w,
+                                          const uint16_t *__restrict__ scales, int cols,
+                                          int64_t n_sub, int64_t i, float (&v)[D])
+{
+    const int64_t r = i / n_sub, j = i - r * n_sub;
+    const float s = half_bits_to_float(scales[r * (cols / 64) + (j * D) / 64]);
+    const uint16_t *src = w + r * cols + j * D;
+#pragma unroll
+    for (int t = 0; t < D; ++t)
+        v[t] = s == 0.0f ? 0.0f : bf16_bits_to_float(src[t]) / s;
+}
+
+// scales[r][g] = fp16(max |w| over the group): one thread per (row, group).
+__global__ __launch_bounds__(kFitThreads) void k_fit_scales(const uint16_t *__restrict__ w,
+                                                            int64_t n_groups, int groups,
+                                                            uint16_t *__restrict__ scales)
+{
+    const int64_t i = (int64_t)blockIdx.x * kFitThreads + threadIdx.x;
+    if (i >= n_groups)
+        return;
+    const uint4 *src = reinterpret_cast<const uint4 *>(w + (i / groups) * groups * 64 +
+                                                       (i % groups) * 64);
+    uint32_t m = 0;   // largest |w| as bf16 magnitude bits (order-preserving)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const uint4 u = src[q];
+        const uint32_t p[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            m = max(m, p[k] & 0x7fffu);
+            m = max(m, (p[k] >> 16) & 0x7fffu);
+        }
+    }
+    scales[i] = float_to_half_bits(bf16_bits_to_float(m));
+}
+
+// The fit set's vectors (xs) and the initial centroids (C).  Indices are
+// clamped into the tensor (a precondition; the clamp keeps reads in bounds).
+template <int D>
+__global__ __launch_bounds__(kFitThreads) void k_fit_vectors(
+    const uint16_t *__restrict__ w, const uint16_t *__restrict__ scales, int cols, int64_t N,
+    const int64_t *__restrict__ sample, int64_t n_sample, const int64_t *__restrict__ init, int K,
+    float *__restrict__ xs, float *__restrict__ C)
+{
+    const int64_t i = (int64_t)blockIdx.x * kFitThreads + threadIdx.x;
+    if (i >= n_sample + K)
+        return;
+    const bool is_init = i >= n_sample;
+    int64_t idx = is_init ? init[i - n_sample] : sample[i];
+    idx = idx < 0 ? 0 : (idx >= N ? N - 1 : idx);
+    float v[D];
+    subvector<D>(w, scales, cols, cols / D, idx, v);
+    float *dst = is_init ? C + (i - n_sample) * D : xs + i * D;
+#pragma unroll
+    for (int t = 0; t < D; ++t)
+        dst[t] = v[t];
+}
+
+__device__ __forceinline__ void stage_centroids(const float *__restrict__ C, int n, float *lds)
+{
+    for (int i = threadIdx.x; i < n; i += kFitThreads)
+        lds[i] = C[i];
+    __syncthreads();
+}
+
+// One assignment pass: every fit-set vector to its nearest centroid, its
+// coordinates added (as integers on the 2^-30 grid) to that centroid's sums.
+template <int D>
+__global__ __launch_bounds__(kFitThreads) void k_lloyd_assign(const float *__restrict__ xs,
+                                                              int64_t n_sample,
+                                                              const float *__restrict__ C, int K,
+                                                              unsigned long long *__restrict__ sums,
+                                                              unsigned long long *__restrict__ cnt)
+{
+    extern __shared__ float cl[];
+    stage_centroids(C, K * D, cl);
+    for (int64_t i = (int64_t)blockIdx.x * kFitThreads + threadIdx.x; i < n_sample;
+         i += (int64_t)gridDim.x * kFitThreads) {
+        float x[D];
+#pragma unroll
+        for (int t = 0; t < D; ++t)
+            x[t] = xs[i * D + t];
+        const uint32_t k = nearest<D>(x, cl, K);
+        atomicAdd(cnt + k, 1ull);
+#pragma unroll
+        for (int t = 0; t < D; ++t) {
+            const long long q = (long long)rint((double)x[t] * 0x1p30);
+            atomicAdd(sums + (int64_t)k * D + t, (unsigned long long)q);
+        }
+    }
+}
+
+// Centroid update from the sums (members' mean; none: unchanged), then the
+// sums are cleared for the next pass.
+__global__ __launch_bounds__(kFitThreads) void k_lloyd_update(float *__restrict__ C, int K, int d,
+                                                              unsigned long long *__restrict__ sums,
+                                                              unsigned long long *__restrict__ cnt)
+{
+    const int k = blockIdx.x * kFitThreads + threadIdx.x;
+    if (k >= K)
+        return;
+    const unsigned long long n = cnt[k];
+    for (int t = 0; t < d; ++t) {
+        if (n != 0) {
+            const long long s = (long long)sums[(int64_t)k * d + t];
+            C[(int64_t)k * d + t] = (float)(((double)s / (double)n) * 0x1p-30);
+        }
+        sums[(int64_t)k * d + t] = 0ull;
+    }
+    cnt[k] = 0ull;
+}
+
+__global__ __launch_bounds__(kFitThreads) void k_fit_clear(unsigned long long *__restrict__ p,
+                                                           int n)
+{
+    const int i = blockIdx.x * kFitThreads + threadIdx.x;
+    if (i < n)
+        p[i] = 0ull;
+}
+
+// codebook = fp16(C); C is then replaced by the fp16 values, which the
+// encode pass searches.
+__global__ __launch_bounds__(kFitThreads) void k_fit_codebook(float *__restrict__ C, int n,
+                                                              uint16_t *__restrict__ codebook)
+{
+    const int i = blockIdx.x * kFitThreads + threadIdx.x;
+    if (i >= n)
+        return;
+    const uint16_t h = float_to_half_bits(C[i]);
+    codebook[i] = h;
+    C[i] = half_bits_to_float(h);
+}
+
+// Encode and pack: one thread per (row, 32-code block), writing the block's
+// BITS words.
+template <int D>
+__global__ __launch_bounds__(kFitThreads) void k_fit_encode(
+    const uint16_t *__restrict__ w, const uint16_t *__restrict__ scales, int64_t n_rows,
+    int cols, int bits, const float *__restrict__ C, int K, uint32_t *__restrict__ codes)
+{
+    extern __shared__ float cl[];
+    stage_centroids(C, K * D, cl);
+    const int64_t n_sub = cols / D;
+    const int n_blk = (int)((n_sub + 31) / 32);
+    const int64_t i = (int64_t)blockIdx.x * kFitThreads + threadIdx.x;
+    if (i >= n_rows * n_blk)
+        return;
+    const int64_t r = i / n_blk;
+    const int blk = (int)(i - r * n_blk);
+    uint32_t *out = codes + r * (int64_t)n_blk * bits + (int64_t)blk * bits;
+    uint64_t acc = 0;
+    int nb = 0;
+    for (int c = 0; c < 32; ++c) {
+        const int64_t j = (int64_t)blk * 32 + c;
+        uint32_t code = 0;   // padding codes past the row's end are zero
+        if (j < n_sub) {
+            float v[D];
+            subvector<D>(w, scales, cols, n_sub, r * n_sub + j, v);
+            code = nearest<D>(v, cl, K);
+        }
+        acc |= (uint64_t)code << nb;
+        nb += bits;
+        if (nb >= 32) {
+            *out++ = (uint32_t)acc;
+            acc >>= 32;
+            nb -= 32;
+        }
+    }
+}
+
+unsigned grid_for(int64_t n) { return (unsigned)std::max<int64_t>(1, (n + kFitThreads - 1) / kFitThreads); }
+
+template <int D>
+hipError_t fit_d(const FitArgs &f, hipStream_t s)
+{
+    const int64_t N = f.n_rows * (f.cols / D);
+    const int groups = f.cols / 64;
+    const int kd = f.K * D;
+    const size_t lds = (size_t)kd * 4;
+    hipLaunchKernelGGL(k_fit_scales, dim3(grid_for(f.n_rows * groups)), dim3(kFitThreads), 0, s,
+                       f.w, f.n_rows * groups, groups, f.scales);
+    hipLaunchKernelGGL(k_fit_vectors<D>, dim3(grid_for(f.n_sample + f.K)), dim3(kFitThreads), 0,
+                       s, f.w, f.scales, f.cols, N, f.sample, f.n_sample, f.init, f.K, f.xs, f.C);
+    hipLaunchKernelGGL(k_fit_clear, dim3(grid_for(kd + f.K)), dim3(kFitThreads), 0, s, f.sums,
+                       kd + f.K);
+    const unsigned assign_grid =
+        (unsigned)std::min<int64_t>(grid_for(f.n_sample), 8 * 256);
+    for (int it = 0; it < f.iters; ++it) {
+        if (f.n_sample > 0)
+            hipLaunchKernelGGL(k_lloyd_assign<D>, dim3(assign_grid), dim3(kFitThreads), lds, s,
+                               f.xs, f.n_sample, f.C, f.K, f.sums, f.sums + kd);
+        hipLaunchKernelGGL(k_lloyd_update, dim3(grid_for(f.K)), dim3(kFitThreads), 0, s, f.C,
+                           f.K, D, f.sums, f.sums + kd);
+    }
+    hipLaunchKernelGGL(k_fit_codebook, dim3(grid_for(kd)), dim3(kFitThreads), 0, s, f.C, kd,
+                       f.codebook);
+    const int n_blk = (int)((f.cols / D + 31) / 32);
+    hipLaunchKernelGGL(k_fit_encode<D>, dim3(grid_for(f.n_rows * n_blk)), dim3(kFitThreads), lds,
+                       s, f.w, f.scales, f.n_rows, f.cols, f.bits, f.C, f.K, f.codes);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t fit_workspace_bytes(int d, int K, int64_t n_sample, FitArgs *f, void *ws)
+{
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    const size_t xs = up((size_t)n_sample * d * 4);
+    const size_t c = up((size_t)K * d * 4);
+    const size_t sums = up(((size_t)K * d + K) * 8);
+    if (f) {
+        char *p = static_cast<char *>(ws);
+        f->xs = reinterpret_cast<float *>(p);
+        f->C = reinterpret_cast<float *>(p + xs);
+        f->sums = reinterpret_cast<unsigned long long *>(p + xs + c);
+    }
+    return xs + c + sums;
+}
+
+hipError_t launch_fit(const FitArgs &f, hipStream_t stream)
+{
+    switch (f.d) {
+    case 2: return fit_d<2>(f, stream);
+    case 4: return fit_d<4>(f, stream);
+    case 8: return fit_d<8>(f, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace vq

@@ -56,6 +56,26 @@ hipError_t launch_combine(const float *z, const float *w, int n_tok, int top_k, 
 
 hipError_t launch_dequantize(const TensorDev &t, int expert, float *w, hipStream_t stream);
 
+// Fitting the format (scales, Lloyd iterations, fp16 codebook, encode).
+struct FitArgs {
+    int64_t n_rows;
+    int cols, d, bits, K;
+    const uint16_t *w;          // bf16 [n_rows][cols]
+    int64_t n_sample;
+    const int64_t *sample;      // [n_sample] subvector indices (the fit set)
+    const int64_t *init;        // [K] subvector indices (initial centroids)
+    int iters;
+    uint16_t *codebook;         // fp16 [K][d] out
+    uint16_t *scales;           // fp16 [n_rows][cols/64] out
+    uint32_t *codes;            // [n_rows][wpr] out
+    float *xs;                  // workspace: fit-set vectors [n_sample][d]
+    float *C;                   // workspace: centroids [K][d]
+    unsigned long long *sums;   // workspace: [K*d] sums, then [K] counts
+};
+// Workspace bytes; with f set, also places f's workspace pointers in ws.
+size_t fit_workspace_bytes(int d, int K, int64_t n_sample, FitArgs *f, void *ws);
+hipError_t launch_fit(const FitArgs &f, hipStream_t stream);
+
 // y[i] = logical row ids[i] (= e*rows + r) of the stacked tensor, fp32.
 hipError_t launch_gather(const TensorDev &t, int64_t n, const int64_t *ids, float *y,
                          hipStream_t stream);

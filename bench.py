@@ -165,6 +165,8 @@ def main():
         return bench_gather(args, synth.GATHER_WORKLOADS[args.workload])
     if args.workload in synth.STACK_WORKLOADS:
         return bench_stack(args, synth.STACK_WORKLOADS[args.workload])
+    if args.workload in synth.FIT_WORKLOADS:
+        return bench_fit(args, synth.FIT_WORKLOADS[args.workload])
     wl = synth.WORKLOADS[args.workload]
     prefill = wl.n_tok > 16
     family = "prefill" if prefill else "decode"
@@ -563,6 +565,119 @@ def bench_stack(args, sw):
             "device_copies": {str(k): v for k, v in copies.items()}, "hip_graph": use_graph,
             "graph_replay_bit_equal": graph_check,
             "peak_frac": round(value / HBM_PEAK_GBS, 4), "bytes_per_step": int(total / K),
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+# MI355X's published fp32 vector peak (256 CUs, 2.4 GHz, 256 flops per CU
+# and clock, counting packed fused multiply-adds)
+VALU_F32_PEAK_TFLOPS = 157.3
+
+
+def bench_fit(args, fw):
+    """Fitting the format to one projection's weights: a step is one vq_fit
+    call (scales, the Lloyd iterations on the fit set, the fp16 codebook and
+    the encode pass over every subvector)."""
+    import numpy as np
+    import torch
+
+    import synth
+    import vq_dequant_matmul_amd as vq
+
+    K = args.steps if args.steps is not None else 5
+    W = args.warmup if args.warmup is not None else 1
+    n_k = args.kernel_launches if args.kernel_launches is not None else 5
+    t0 = time.perf_counter()
+    w = synth.make_fit_weights(fw.seed, fw.n_rows, fw.cols)
+    sample, init = fw.draws()
+    w_dev = torch.from_numpy(w.view(np.int16)).cuda().view(torch.bfloat16)
+    s_dev, i_dev = torch.from_numpy(sample).cuda(), torch.from_numpy(init).cuda()
+    ws_bytes = vq.load_library().vq_fit_workspace_size(fw.d, fw.K, fw.n_sample)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] {fw.name}: {fw.n_rows}x{fw.cols} bf16 weights, fit set {fw.n_sample}, "
+        f"K={fw.K}, {fw.iters} iterations, setup {time.perf_counter() - t0:.1f}s")
+    N = fw.n_rows * (fw.cols // fw.d)
+    # subtract, multiply, add per coordinate of every subvector-entry pair
+    assign_flops = fw.iters * fw.n_sample * fw.K * fw.d * 3
+    encode_flops = N * fw.K * fw.d * 3
+    step_flops = assign_flops + encode_flops
+
+    out = {}
+
+    def step():
+        out["r"] = vq.vq_fit(w_dev, fw.d, fw.bits, fw.K, s_dev, i_dev, fw.iters, workspace=ws)
+
+    for _ in range(W):
+        step()
+    torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    log(f"[bench] timed {K} fits in {elapsed * 1e3:.2f} ms")
+    value = step_flops * K / elapsed / 1e12
+
+    hip = HipEvents()
+    pairs = [(hip.create(), hip.create()) for _ in range(n_k)]
+    for j in range(n_k):
+        vq.vq_set_kernel_events(pairs[j][0], pairs[j][1])
+        step()
+    vq.vq_set_kernel_events(None, None)
+    torch.cuda.synchronize()
+    durs = np.array([hip.elapsed_ms(a, b) * 1e-3 for a, b in pairs])
+    for a, b in pairs:
+        hip.destroy(a)
+        hip.destroy(b)
+    k_mean = float(durs.mean())
+    achieved = encode_flops / k_mean / 1e12
+    roofline = {"bound": "alu", "achieved": round(achieved, 2),
+                "peak": round(VALU_F32_PEAK_TFLOPS, 1), "unit": "TFLOP/s",
+                "frac": round(achieved / VALU_F32_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": "vq::k_fit_encode (nearest fp16 entry for every subvector, packed)",
+                "launch_us": round(k_mean * 1e6, 2), "flops_per_launch": int(encode_flops),
+                "timing": f"HIP event pair around each of {n_k} launches"}
+    log(f"[bench] encode: {k_mean * 1e3:.3f} ms/launch, {achieved:.2f} TFLOP/s")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        import oracle
+        oracle.build(force=False)
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        # a bounded slice: the first rows of the tensor with a proportional
+        # share of the fit set (its indices that fall in those rows)
+        rows = 1024
+        n_sub = fw.cols // fw.d
+        sub_s = sample[sample < rows * n_sub]
+        sub_i = init % (rows * n_sub)
+        t_cpu, n_cpu, work = 0.0, 0, 0
+        while t_cpu < args.cpu_seconds and n_cpu < 1000:
+            c0 = time.perf_counter()
+            oracle.fit(w[:rows], fw.d, fw.bits, fw.K, sub_s, sub_i, fw.iters)
+            t_cpu += time.perf_counter() - c0
+            work += (fw.iters * len(sub_s) + rows * n_sub) * fw.K * fw.d * 3
+            n_cpu += 1
+        cpu = {"value": round(work / t_cpu / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+               "kind": "oracle",
+               "sample": f"{n_cpu} fits of the first {rows} rows with their share of the fit "
+                         f"set ({len(sub_s)} subvectors), {t_cpu:.1f}s"}
+        log(f"[bench] cpu oracle: {n_cpu} fits in {t_cpu:.1f}s")
+
+    rec = {
+        "metric": "VQ codebook fit TFLOP/s (nearest-entry searches, % fp32 VALU peak)",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(elapsed * 1e3 / K, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {
+            "workload": fw.name, "rows": fw.n_rows, "cols": fw.cols, "d": fw.d,
+            "bits": fw.bits, "K": fw.K, "fit_set": fw.n_sample, "iterations": fw.iters,
+            "seed": fw.seed, "subvectors": N, "flops_per_step": int(step_flops),
+            "peak_frac": round(value / VALU_F32_PEAK_TFLOPS, 4),
         },
         "roofline": roofline,
         "cpu_baseline": cpu,

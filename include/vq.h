@@ -252,9 +252,10 @@ vq_status vq_fit(int64_t n_rows, int32_t cols, int32_t d, int32_t bits, int32_t 
 /* ---- measurement -------------------------------------------------------------- */
 
 /* Until cleared (NULL, NULL), every vq_moe_ffn / vq_moe_gate_up /
-   vq_expert_gemm call made on this thread records `start` (a hipEvent_t)
-   on its stream right before its dominant kernel (the fused gate+up launch;
-   the GEMM for vq_expert_gemm) and `stop` right after it, so a caller can
+   vq_expert_gemm / vq_fit call made on this thread records `start` (a
+   hipEvent_t) on its stream right before its dominant kernel (the fused
+   gate+up launch; the GEMM for vq_expert_gemm; the encode pass for vq_fit)
+   and `stop` right after it, so a caller can
    time that one kernel with hipEventElapsedTime.  The events are owned by
    the caller. */
 vq_status vq_set_kernel_events(void *start, void *stop);

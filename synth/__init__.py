@@ -386,6 +386,36 @@ def make_stack_layer(sw: StackWorkload, layer: int):
 # (a heavier tail, as trained weights have), rounded to bf16.
 # --------------------------------------------------------------------------
 
+@dataclass(frozen=True)
+class FitWorkload:
+    name: str
+    n_rows: int
+    cols: int
+    d: int
+    bits: int
+    K: int
+    n_sample: int
+    iters: int
+    seed: int = 1234          # the seed the GLM and Flash-Next cards fit with
+
+    def draws(self):
+        """The fit set (sorted subvector indices, without replacement) and the
+        K initial subvectors, drawn with the workload's seed."""
+        g = rng_for(self.seed, 70_000)
+        N = self.n_rows * (self.cols // self.d)
+        sample = np.sort(g.choice(N, self.n_sample, replace=False)).astype(np.int64)
+        init = g.choice(N, self.K, replace=False).astype(np.int64)
+        return sample, init
+
+
+FIT_WORKLOADS = {
+    # one gate projection of the 128-expert layer (128 x 768 rows of 2048),
+    # d=4/K=512, a 2^20-subvector fit set, 10 Lloyd iterations
+    "fit_e128_gate_h2048_i768_d4k512": FitWorkload(
+        "fit_e128_gate_h2048_i768_d4k512", 128 * 768, 2048, 4, 9, 512, 1 << 20, 10),
+}
+
+
 def make_fit_weights(seed: int, n_rows: int, cols: int) -> np.ndarray:
     """bf16 bit patterns [n_rows, cols]."""
     g = rng_for(seed, 60_000)

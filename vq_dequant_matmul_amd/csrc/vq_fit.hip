@@ -276,9 +276,15 @@ hipError_t fit_d(const FitArgs &f, hipStream_t s)
     hipLaunchKernelGGL(k_fit_codebook, dim3(grid_for(kd)), dim3(kFitThreads), 0, s, f.C, kd,
                        f.codebook);
     const int n_blk = (int)((f.cols / D + 31) / 32);
+    const KernelEvents &ev = kernel_events();
+    if (ev.start)
+        (void)hipEventRecord(ev.start, s);
     hipLaunchKernelGGL(k_fit_encode<D>, dim3(grid_for(f.n_rows * n_blk)), dim3(kFitThreads), lds,
                        s, f.w, f.scales, f.n_rows, f.cols, f.bits, f.C, f.K, f.codes);
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (ev.stop)
+        (void)hipEventRecord(ev.stop, s);
+    return e;
 }
 
 }  // namespace

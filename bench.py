@@ -103,13 +103,13 @@ class HipEvents:
 
 
 def kernel_source_hash(family: str) -> str:
-    """Hash of the sources that build one kernel family ("decode" or
-    "prefill"); recorded counter traffic is valid only for that hash."""
+    """Hash of the device sources that build one kernel family ("decode",
+    "prefill", "gather": its own files and the shared device header);
+    recorded counter traffic is valid only for that hash."""
     import hashlib
     h = hashlib.sha256()
     for name in sorted(os.listdir(CSRC)):
-        if name.startswith("vq_" + family) or name in ("vq_common.hpp", "vq_internal.hpp",
-                                                       "vq_api.cpp"):
+        if name.startswith("vq_" + family) or name == "vq_common.hpp":
             with open(os.path.join(CSRC, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]

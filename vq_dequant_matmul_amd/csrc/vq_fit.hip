@@ -22,7 +22,7 @@
 //     row-local 32-code blocks.
 // All of it is ALU work on small data: nearest-centroid searches against a
 // codebook held in LDS (K*d fp32 values), K*d subtract-multiply-add triples
-// per subvector.
+// per subvector; the weights are read once, coalesced.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -212,40 +212,52 @@ __global__ __launch_bounds__(kFitThreads) void k_fit_codebook(float *__restrict_
     C[i] = half_bits_to_float(h);
 }
 
-// Encode and pack: one thread per (row, 32-code block), writing the block's
-// BITS words.
+// Encode and pack.  A workgroup takes kEncBlocks consecutive 32-code blocks
+// (in row-major block order, which is also the order of their words in
+// memory); thread t codes subvector t % 32 of block t / 32, so a wavefront
+// reads its blocks' weights contiguously.  The codes meet in LDS, and one
+// thread per output word then gathers the codes overlapping its 32 bits,
+// so the blocks' words are written contiguously too.
+constexpr int kEncBlocks = kFitThreads / 32;
+
 template <int D>
 __global__ __launch_bounds__(kFitThreads) void k_fit_encode(
     const uint16_t *__restrict__ w, const uint16_t *__restrict__ scales, int64_t n_rows,
     int cols, int bits, const float *__restrict__ C, int K, uint32_t *__restrict__ codes)
 {
     extern __shared__ float cl[];
+    __shared__ uint32_t cs[kFitThreads];
     stage_centroids(C, K * D, cl);
     const int64_t n_sub = cols / D;
     const int n_blk = (int)((n_sub + 31) / 32);
-    const int64_t i = (int64_t)blockIdx.x * kFitThreads + threadIdx.x;
-    if (i >= n_rows * n_blk)
-        return;
-    const int64_t r = i / n_blk;
-    const int blk = (int)(i - r * n_blk);
-    uint32_t *out = codes + r * (int64_t)n_blk * bits + (int64_t)blk * bits;
-    uint64_t acc = 0;
-    int nb = 0;
-    for (int c = 0; c < 32; ++c) {
-        const int64_t j = (int64_t)blk * 32 + c;
-        uint32_t code = 0;   // padding codes past the row's end are zero
+    const int64_t n_blocks = n_rows * n_blk;
+    const int64_t b0 = (int64_t)blockIdx.x * kEncBlocks;
+    const int t = threadIdx.x;
+    const int64_t bi = b0 + t / 32;          // this thread's block (row-major)
+    uint32_t code = 0;                       // padding codes past the row's end are zero
+    if (bi < n_blocks) {
+        const int64_t r = bi / n_blk;
+        const int64_t j = (bi - r * n_blk) * 32 + (t & 31);
         if (j < n_sub) {
             float v[D];
             subvector<D>(w, scales, cols, n_sub, r * n_sub + j, v);
             code = nearest<D>(v, cl, K);
         }
-        acc |= (uint64_t)code << nb;
-        nb += bits;
-        if (nb >= 32) {
-            *out++ = (uint32_t)acc;
-            acc >>= 32;
-            nb -= 32;
+    }
+    cs[t] = code;
+    __syncthreads();
+    // word q of local block lb holds stream bits [32q, 32q + 32) of that
+    // block: codes floor(32q/bits) .. floor((32q+31)/bits)
+    const int64_t nb = min((int64_t)kEncBlocks, n_blocks - b0);
+    for (int o = t; o < nb * bits; o += kFitThreads) {
+        const int lb = o / bits, q = o - lb * bits;
+        const uint32_t *bc = cs + lb * 32;
+        uint32_t word = 0;
+        for (int c = (32 * q) / bits; c < 32 && c * bits < 32 * q + 32; ++c) {
+            const int sh = c * bits - 32 * q;   // code c's offset from this word's bit 0
+            word |= sh >= 0 ? bc[c] << sh : bc[c] >> -sh;
         }
+        codes[b0 * bits + o] = word;
     }
 }
 
@@ -276,11 +288,14 @@ hipError_t fit_d(const FitArgs &f, hipStream_t s)
     hipLaunchKernelGGL(k_fit_codebook, dim3(grid_for(kd)), dim3(kFitThreads), 0, s, f.C, kd,
                        f.codebook);
     const int n_blk = (int)((f.cols / D + 31) / 32);
+    const int64_t enc_grid = (f.n_rows * n_blk + kEncBlocks - 1) / kEncBlocks;
+    if (enc_grid > 0x7fffffff)
+        return hipErrorInvalidValue;
     const KernelEvents &ev = kernel_events();
     if (ev.start)
         (void)hipEventRecord(ev.start, s);
-    hipLaunchKernelGGL(k_fit_encode<D>, dim3(grid_for(f.n_rows * n_blk)), dim3(kFitThreads), lds,
-                       s, f.w, f.scales, f.n_rows, f.cols, f.bits, f.C, f.K, f.codes);
+    hipLaunchKernelGGL(k_fit_encode<D>, dim3((unsigned)enc_grid), dim3(kFitThreads), lds, s, f.w,
+                       f.scales, f.n_rows, f.cols, f.bits, f.C, f.K, f.codes);
     const hipError_t e = hipGetLastError();
     if (ev.stop)
         (void)hipEventRecord(ev.stop, s);

@@ -146,7 +146,12 @@ __device__ __forceinline__ void stage_centroids(const float *__restrict__ C, int
 
 // One assignment pass: every fit-set vector to its nearest centroid, its
 // coordinates added (as integers on the 2^-30 grid) to that centroid's sums.
-template <int D>
+// LOCAL: the workgroup first adds into its own sums in LDS (after the
+// centroids) and then adds those to the global ones, one atomic per
+// non-zero sum, so a hot centroid costs each workgroup one global atomic
+// instead of one per member.  Either way the sums are exact integers, so the
+// result is the same.
+template <int D, bool LOCAL>
 __global__ __launch_bounds__(kFitThreads) void k_lloyd_assign(const float *__restrict__ xs,
                                                               int64_t n_sample,
                                                               const float *__restrict__ C, int K,
@@ -154,7 +159,14 @@ __global__ __launch_bounds__(kFitThreads) void k_lloyd_assign(const float *__res
                                                               unsigned long long *__restrict__ cnt)
 {
     extern __shared__ float cl[];
-    stage_centroids(C, K * D, cl);
+    unsigned long long *ls = reinterpret_cast<unsigned long long *>(cl + ((K * D + 1) & ~1));
+    unsigned long long *lc = ls + K * D;
+    if constexpr (LOCAL)
+        for (int i = threadIdx.x; i < K * D + K; i += kFitThreads)
+            ls[i] = 0ull;
+    stage_centroids(C, K * D, cl);   // ends with a barrier
+    unsigned long long *ts = LOCAL ? ls : sums;
+    unsigned long long *tc = LOCAL ? lc : cnt;
     for (int64_t i = (int64_t)blockIdx.x * kFitThreads + threadIdx.x; i < n_sample;
          i += (int64_t)gridDim.x * kFitThreads) {
         float x[D];
@@ -162,11 +174,19 @@ __global__ __launch_bounds__(kFitThreads) void k_lloyd_assign(const float *__res
         for (int t = 0; t < D; ++t)
             x[t] = xs[i * D + t];
         const uint32_t k = nearest<D>(x, cl, K);
-        atomicAdd(cnt + k, 1ull);
+        atomicAdd(tc + k, 1ull);
 #pragma unroll
         for (int t = 0; t < D; ++t) {
             const long long q = (long long)rint((double)x[t] * 0x1p30);
-            atomicAdd(sums + (int64_t)k * D + t, (unsigned long long)q);
+            atomicAdd(ts + (int64_t)k * D + t, (unsigned long long)q);
+        }
+    }
+    if constexpr (LOCAL) {
+        __syncthreads();
+        for (int i = threadIdx.x; i < K * D + K; i += kFitThreads) {
+            const unsigned long long v = ls[i];
+            if (v != 0ull)
+                atomicAdd(i < K * D ? sums + i : cnt + (i - K * D), v);
         }
     }
 }
@@ -261,6 +281,22 @@ __global__ __launch_bounds__(kFitThreads) void k_fit_encode(
     }
 }
 
+int device_cus()
+{
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 unsigned grid_for(int64_t n) { return (unsigned)std::max<int64_t>(1, (n + kFitThreads - 1) / kFitThreads); }
 
 template <int D>
@@ -276,12 +312,21 @@ hipError_t fit_d(const FitArgs &f, hipStream_t s)
                        s, f.w, f.scales, f.cols, N, f.sample, f.n_sample, f.init, f.K, f.xs, f.C);
     hipLaunchKernelGGL(k_fit_clear, dim3(grid_for(kd + f.K)), dim3(kFitThreads), 0, s, f.sums,
                        kd + f.K);
-    const unsigned assign_grid =
-        (unsigned)std::min<int64_t>(grid_for(f.n_sample), 8 * 256);
+    // per-workgroup sums in LDS when they fit beside the centroids (then a
+    // few workgroups per CU, each with many members); else global atomics
+    const size_t lds_local = (size_t)((kd + 1) & ~1) * 4 + (size_t)(kd + f.K) * 8;
+    const bool local = lds_local <= 65536;
+    const unsigned assign_grid = (unsigned)std::min<int64_t>(
+        grid_for(f.n_sample), local ? 2 * (int64_t)device_cus() : 8 * 256);
     for (int it = 0; it < f.iters; ++it) {
-        if (f.n_sample > 0)
-            hipLaunchKernelGGL(k_lloyd_assign<D>, dim3(assign_grid), dim3(kFitThreads), lds, s,
-                               f.xs, f.n_sample, f.C, f.K, f.sums, f.sums + kd);
+        if (f.n_sample > 0) {
+            if (local)
+                hipLaunchKernelGGL((k_lloyd_assign<D, true>), dim3(assign_grid), dim3(kFitThreads),
+                                   lds_local, s, f.xs, f.n_sample, f.C, f.K, f.sums, f.sums + kd);
+            else
+                hipLaunchKernelGGL((k_lloyd_assign<D, false>), dim3(assign_grid), dim3(kFitThreads),
+                                   lds, s, f.xs, f.n_sample, f.C, f.K, f.sums, f.sums + kd);
+        }
         hipLaunchKernelGGL(k_lloyd_update, dim3(grid_for(f.K)), dim3(kFitThreads), 0, s, f.C,
                            f.K, D, f.sums, f.sums + kd);
     }

@@ -27,7 +27,7 @@ namespace vq {
 namespace {
 
 constexpr int kThreadsG = 256;
-constexpr int kUnroll = 4;
+
 
 struct GatherArgs {
     const uint32_t *codes;
@@ -47,7 +47,7 @@ struct GatherArgs {
 
 // One output chunk: columns [4*c4, 4*c4 + 4) of the row named by ids[j].
 // D=2 takes two codes, D=4 one, D=8 one half of a code's 8-vector.
-template <int D, int BITS>
+template <int D, int BITS, int kUnroll>
 __global__ __launch_bounds__(kThreadsG) void k_gather(GatherArgs a)
 {
     constexpr int NC = D == 2 ? 2 : 1;      // codes per chunk
@@ -182,19 +182,32 @@ int device_cus()
     return cached[dev];
 }
 
+template <int D, int BITS, int U>
+hipError_t gather_launch(const GatherArgs &a, hipStream_t stream)
+{
+    const size_t lds = (size_t)a.cb_dwords * 4;
+    // Small codebooks: one batch of U chunks per thread, workgroups queued
+    // in output order (a measured few per cent ahead of a resident grid).
+    // Codebooks over 4 KiB: as many resident workgroups as the LDS allows,
+    // up to 8 per CU, and a grid-stride loop, so that each stages its
+    // codebook once for many chunks.
+    const int per_cu = lds == 0 ? 8 : (int)std::max<size_t>(1, std::min<size_t>(8, 163840 / lds));
+    const uint64_t want = (a.n_chunks + (uint64_t)kThreadsG * U - 1) / ((uint64_t)kThreadsG * U);
+    const uint64_t cap = lds <= 4096 ? want : (uint64_t)per_cu * device_cus();
+    const unsigned blocks = (unsigned)std::max<uint64_t>(1, std::min(want, cap));
+    hipLaunchKernelGGL((k_gather<D, BITS, U>), dim3(blocks), dim3(kThreadsG), lds, stream, a);
+    return hipGetLastError();
+}
+
+// Eight chunks per thread keep enough loads in flight on large gathers; a
+// gather too small to fill the chip with such batches (a token's lookups)
+// takes one chunk per thread, which shortens each thread's chain.
 template <int D, int BITS>
 hipError_t gather_db(const GatherArgs &a, hipStream_t stream)
 {
-    const size_t lds = (size_t)a.cb_dwords * 4;
-    // as many resident workgroups as the LDS allows, up to 8 per CU
-    // (32 wavefronts), then a grid-stride loop
-    const int per_cu = lds == 0 ? 8 : (int)std::max<size_t>(1, std::min<size_t>(8, 163840 / lds));
-    const uint64_t want = (a.n_chunks + (uint64_t)kThreadsG * kUnroll - 1) /
-                          ((uint64_t)kThreadsG * kUnroll);
-    const uint64_t cap = (uint64_t)per_cu * device_cus();
-    const unsigned blocks = (unsigned)std::max<uint64_t>(1, std::min(want, cap));
-    hipLaunchKernelGGL((k_gather<D, BITS>), dim3(blocks), dim3(kThreadsG), lds, stream, a);
-    return hipGetLastError();
+    if (a.n_chunks < (uint64_t)kThreadsG * 8 * device_cus())
+        return gather_launch<D, BITS, 1>(a, stream);
+    return gather_launch<D, BITS, 8>(a, stream);
 }
 
 template <int D>

@@ -347,7 +347,7 @@ def main():
         cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
         t_cpu, n_cpu, work = 0.0, 0, 0
         rng = np.random.default_rng(0)
-        while t_cpu < args.cpu_seconds and n_cpu < n_steps:
+        while t_cpu < args.cpu_seconds and n_cpu < 10 * n_steps:
             i = W + n_cpu % K
             if prefill:
                 # a few tokens of the step: each token's output is independent
@@ -801,7 +801,7 @@ def bench_gather(args, wl):
         oracle.build(force=False)
         cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
         t_cpu, n_cpu = 0.0, 0
-        while t_cpu < args.cpu_seconds and n_cpu < n_steps:
+        while t_cpu < args.cpu_seconds and n_cpu < 10 * n_steps:
             c0 = time.perf_counter()
             oracle.gather(T, ids[W + n_cpu % K])
             t_cpu += time.perf_counter() - c0

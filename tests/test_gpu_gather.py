@@ -154,3 +154,21 @@ def test_gather_full_size_sampled():
     got = y[torch.from_numpy(pick).cuda()].cpu().numpy()
     assert _same_bits(got, oracle.gather(T, ids[pick]))
     assert bool(torch.isfinite(y).all())
+
+
+@pytest.mark.parametrize("d,bits,K,dead", [(4, 13, 8192, 5), (2, 8, 256, 0)])
+def test_gather_large_batches(d, bits, K, dead):
+    """Gathers large enough for eight chunks per thread, with a small
+    codebook (queued grid) and a 64 KiB one (resident grid-stride launch):
+    every row against the oracle."""
+    rows, E, cols = 400, 8, 256
+    T = synth.make_tensor(48, d * 100 + bits, rows=rows, cols=cols, d=d, bits=bits, K=K,
+                          n_experts=E, dead_rows=dead)
+    W = vq.VQTensor.from_host(T)
+    n = 12011                                   # 768704 chunks of 4 columns
+    ids = np.random.default_rng(bits).integers(-2, E * rows + 2, size=n).astype(np.int64)
+    got = _gather(T, W, ids)
+    ref = oracle.gather(T, ids)
+    bad = (ids < 0) | (ids >= E * rows)
+    assert np.isnan(got[bad]).all()
+    assert _same_bits(got[~bad], ref[~bad])

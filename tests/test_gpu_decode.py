@@ -171,6 +171,20 @@ def test_moe_decode_small(T, E, k, d, bits, dead):
     check_close(y, oracle.moe_ffn(gate, up, down, x, ids, w), "small moe")
 
 
+@pytest.mark.parametrize("T,E,k,H,I", [
+    (16, 64, 64, 128, 64),     # n_tokens * top_k = 1024, the routed-list maximum
+    (2, 4, 2, 8192, 64),       # hidden 8192: 128 groups per row, the decode maximum
+])
+def test_moe_decode_maximum_sizes(T, E, k, H, I):
+    wl = synth.MoEWorkload("max", E, k, H, I, 4, 9, T, seed=90 + T)
+    gate = synth.make_tensor(wl.seed, 1, rows=I, cols=H, d=4, bits=9, n_experts=E, dead_rows=3)
+    up = synth.make_tensor(wl.seed, 2, rows=I, cols=H, d=4, bits=9, n_experts=E)
+    down = synth.make_tensor(wl.seed, 3, rows=H, cols=I, d=4, bits=9, n_experts=E, dead_rows=5)
+    x, ids, w = synth.make_moe_inputs(wl, 0)
+    y = _run_moe(gate, up, down, x, ids, w)
+    check_close(y, oracle.moe_ffn(gate, up, down, x, ids, w), f"max T={T} k={k} H={H}")
+
+
 def test_moe_decode_repeated_expert_in_token():
     """An id repeated within a token is served as two slots of one expert."""
     E, k, H, I = 4, 3, 128, 64

@@ -25,6 +25,14 @@ the three projections) against the 2.5 PFLOP/s dense fp16 MFMA peak.
 ``roofline`` times the dominant kernel (the fused gate+up launch) per
 launch with HIP events recorded on its own stream; ``cpu_baseline`` times
 the CPU oracle on a bounded sample of the same workload on the host cores.
+
+Three more workload families share the JSON line's format: ``moe_stack*``
+(one token through a stack of 40 or 42 MoE layers with promoted layers,
+``vq_moe_stack``), ``ple_gather*`` (rows of stacked VQ embedding tables,
+``vq_row_gather``) and ``fit*`` (fitting the format to one projection's
+bf16 weights, ``vq_fit``, reported in TFLOP/s of nearest-entry searches
+against the fp32 vector peak).  ``--gpus`` above 1 is refused: the path
+runs on one GPU.
 """
 from __future__ import annotations
 

@@ -83,3 +83,31 @@ def test_fit_one_expert_projection():
     # tail add to it
     err = np.linalg.norm(deq - wf) / np.linalg.norm(wf)
     assert 0.21 < err < 0.35, err
+
+
+def test_fit_full_size_sampled():
+    """The benchmarked fit (one 98304 x 2048 gate projection, d4/K512, a 2^20
+    fit set, 10 iterations) as the benchmark calls it: every scale and every
+    codebook entry bit for bit, and the packed codes of 256 sampled rows."""
+    fw = synth.FIT_WORKLOADS["fit_e128_gate_h2048_i768_d4k512"]
+    w = synth.make_fit_weights(fw.seed, fw.n_rows, fw.cols)
+    sample, init = fw.draws()
+    wt = torch.from_numpy(w.view(np.int16)).cuda().view(torch.bfloat16)
+    ws = torch.empty(vq.load_library().vq_fit_workspace_size(fw.d, fw.K, fw.n_sample),
+                     dtype=torch.uint8, device="cuda")
+    cb, sc, codes = vq.vq_fit(wt, fw.d, fw.bits, fw.K, torch.from_numpy(sample).cuda(),
+                              torch.from_numpy(init).cuda(), fw.iters, workspace=ws)
+    torch.cuda.synchronize()
+    cb = cb.cpu().numpy().view(np.uint16)
+    sc = sc.cpu().numpy().view(np.uint16)
+    codes = codes.cpu().numpy().view(np.uint32)
+    del wt
+
+    rsc = oracle.fit_scales(w)
+    assert np.array_equal(sc, rsc)
+    C = oracle.kmeans(w, rsc, fw.d, fw.K, sample, init, fw.iters)
+    rcb = C.astype(np.float16).view(np.uint16)
+    assert np.array_equal(cb, rcb)
+    rows = np.sort(np.random.default_rng(fw.seed).choice(fw.n_rows, 256, replace=False))
+    rcodes = oracle.encode(w[rows], rsc[rows], rcb, fw.d, fw.bits)
+    assert np.array_equal(codes[rows], rcodes)

@@ -223,3 +223,22 @@ def test_fit_reconstruction_error_is_small():
     wf = _bf16_to_f32(w).reshape(n, cols).astype(np.float64)
     err = np.linalg.norm(oracle.decode(T, 0) - wf) / np.linalg.norm(wf)
     assert err < 0.12, err
+
+
+def test_fit_is_its_steps_composed():
+    """The whole fit equals scales, then k-means, then each centroid rounded
+    to fp16 (round to nearest even, numpy's conversion), then encode: the
+    large fit is checked step by step on that basis."""
+    d, bits, K, n, cols = 4, 9, 64, 40, 256
+    w = _weights(16, n, cols)
+    g = np.random.default_rng(17)
+    N = n * cols // d
+    sample = np.sort(g.choice(N, 2000, replace=False))
+    init = g.choice(N, K, replace=False)
+    cb, sc, packed = oracle.fit(w, d, bits, K, sample, init, 4)
+    sc2 = oracle.fit_scales(w)
+    C = oracle.kmeans(w, sc2, d, K, sample, init, 4)
+    cb2 = C.astype(np.float16).view(np.uint16)
+    assert np.array_equal(sc, sc2)
+    assert np.array_equal(cb, cb2)
+    assert np.array_equal(packed, oracle.encode(w, sc2, cb2, d, bits))

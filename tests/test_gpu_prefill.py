@@ -115,3 +115,71 @@ def test_moe_prefill_deterministic():
     a = _run_moe(gate, up, down, x, ids, w)
     b = _run_moe(gate, up, down, x, ids, w)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def _layer(seed, E, H, I, d, bits, dead=(0, 0, 0)):
+    return (synth.make_tensor(seed, 1, rows=I, cols=H, d=d, bits=bits, n_experts=E,
+                              dead_rows=dead[0]),
+            synth.make_tensor(seed, 2, rows=I, cols=H, d=d, bits=bits, n_experts=E,
+                              dead_rows=dead[1]),
+            synth.make_tensor(seed, 3, rows=H, cols=I, d=d, bits=bits, n_experts=E,
+                              dead_rows=dead[2]))
+
+
+def test_moe_prefill_hot_experts_and_repeated_ids():
+    """Every token routed to two of three hot experts out of 32 (several M
+    tiles per hot expert while the tile size follows the mean load, the
+    other 29 experts empty), and every seventh token names one expert in
+    both slots."""
+    T, E, k, H, I = 300, 32, 2, 256, 192
+    gate, up, down = _layer(95, E, H, I, 4, 9)
+    t = np.arange(T)
+    ids = np.stack([t % 3, (t + 1) % 3], axis=1).astype(np.int32)
+    ids[::7, 1] = ids[::7, 0]
+    w = np.random.default_rng(96).random((T, k)).astype(np.float32)
+    x = synth.make_x(95, 4, T, H, "bf16")
+    y = _run_moe(gate, up, down, x, ids, w)
+    check_close(y, oracle.moe_ffn(gate, up, down, x, ids, w), "hot experts")
+
+
+def test_moe_prefill_top1():
+    T, E, k, H, I = 300, 16, 1, 384, 256
+    gate, up, down = _layer(97, E, H, I, 2, 10)
+    x = synth.make_x(97, 4, T, H, "bf16")
+    ids, w = synth.make_routes(97, 5, T, E, k)
+    y = _run_moe(gate, up, down, x, ids, w)
+    check_close(y, oracle.moe_ffn(gate, up, down, x, ids, w), "top-1")
+
+
+class _NoStoredRows(vq.VQTensor):
+    n_stored = property(lambda self: 0)
+
+
+def _dev_all_dead(T):
+    """An all-dead tensor stores nothing: the library gets non-null one-row
+    placeholder arrays and n_stored = 0."""
+    assert T.n_stored == 0
+    T.codes = np.zeros((1, T.codes.shape[1]), np.uint32)
+    T.scales = np.zeros((1, T.scales.shape[1]), np.uint16)
+    D = _dev(T)
+    return _NoStoredRows(D.rows, D.cols, D.d, D.bits, D.K, D.n_experts, D.codebook, D.codes,
+                         D.scales, D.row_map)
+
+
+@pytest.mark.parametrize("which", ["gate", "down"])
+def test_moe_prefill_all_rows_dead(which):
+    """A projection that stores no rows: with down dead every output is
+    exactly +0.0; with gate dead, h = silu(0) * up is zero and so is y."""
+    T, E, k, H, I = 64, 8, 2, 256, 128
+    dead = (I, 0, 0) if which == "gate" else (0, 0, H)
+    gate, up, down = _layer(98, E, H, I, 4, 9, dead)
+    x = synth.make_x(98, 4, T, H, "bf16")
+    ids, w = synth.make_routes(98, 5, T, E, k)
+    ref = oracle.moe_ffn(gate, up, down, x, ids, w)
+    G = _dev_all_dead(gate) if which == "gate" else _dev(gate)
+    D = _dev_all_dead(down) if which == "down" else _dev(down)
+    y = vq.vq_moe_ffn(G, _dev(up), D, x_to_torch(x), torch.from_numpy(ids).cuda(),
+                      torch.from_numpy(w).cuda()).cpu().numpy()
+    assert np.all(ref == 0) and np.all(y == 0)
+    if which == "down":
+        assert np.all(y.view(np.uint32) == 0)

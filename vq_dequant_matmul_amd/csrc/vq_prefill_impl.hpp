@@ -43,12 +43,19 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // 16-byte lane stride (lds_wave_base must be wave-uniform).  Issued as inline assembly: the ring below tracks these loads with its own
 // vmcnt waits, so the compiler must not add blanket waits of its own before
 // every LDS read.  The instruction has no register results.
+// The 32-bit LDS address of a pointer into LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void *p)
+{
+    return (uint32_t)(uintptr_t)(const lds_void_t *)p;
+}
+
+// lds_wave_base: a wave-uniform LDS address, best computed from uniform
+// values only, so that it stays in scalar registers.
 template <int SIZE>
-__device__ __forceinline__ void dma(const void *src, void *lds_wave_base)
+__device__ __forceinline__ void dma(const void *src, uint32_t lds_wave_base)
 {
     static_assert(SIZE == 4 || SIZE == 12 || SIZE == 16, "unsupported load size");
-    const uint32_t m0 =
-        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t *)lds_wave_base);
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
     if constexpr (SIZE == 16)
         asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(src), "{m0}"(m0) : "memory");
     else if constexpr (SIZE == 12)
@@ -179,6 +186,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
     char *const lb = reinterpret_cast<char *>(lds);
     __shared__ __attribute__((aligned(16))) char ring[S * SH::STAGE];
+    const uint32_t lb_l = lds_addr(lb);     // LDS addresses of the two regions
+    const uint32_t ring_l = lds_addr(ring);
 
     // Workgroup L runs on XCD L % 8 (round-robin dispatch); all weight-row
     // tiles of M tile t run on XCD t % 8 one after another, so the tile's
@@ -192,7 +201,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases in SGPRs
     const int h = lane >> 5;
     const int e = a.tiles[3 * tile + 0];
     const int m0 = a.tiles[3 * tile + 1];
@@ -207,10 +216,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
     for (int p = 0; p < NPROJ; ++p) {
         const char *src = reinterpret_cast<const char *>(a.codebook[p]);
         char *dst = lb + a.cb_off[p];
+        const uint32_t dst_l = lb_l + (uint32_t)a.cb_off[p];
         const int n16 = a.cb_bytes[p] >> 4;
         for (int i0 = 0; i0 < n16; i0 += NT)
             if (i0 + tid < n16)
-                dma<16>(src + (size_t)(i0 + tid) * 16, dst + (size_t)(i0 + wave * 64) * 16);
+                dma<16>(src + (size_t)(i0 + tid) * 16, dst_l + (uint32_t)(i0 + wave * 64) * 16u);
         for (int i = (n16 << 2) + tid; i < (a.cb_bytes[p] >> 2); i += NT)
             reinterpret_cast<uint32_t *>(dst)[i] = reinterpret_cast<const uint32_t *>(src)[i];
     }
@@ -256,11 +266,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
     // ---- loads of one stage, one instruction per unit: per (projection, block)
     // the scale and the code window, then the activation rows ---------------------------
     constexpr int PB = BW::NDMA + 1;                     // loads per (projection, block)
-    auto dma_unit = [&](auto Q, int gg, char *sb) {
+    auto dma_unit = [&](auto Q, int gg, uint32_t sb) {
         constexpr int q = decltype(Q)::value;
         if constexpr (q < NPB * PB) {
             constexpr int pb = q / PB, r = q % PB;
-            char *bb = sb + SH::A_BYTES + pb * SH::WIN;
+            const uint32_t bb = sb + SH::A_BYTES + pb * SH::WIN;
             if constexpr (r == 0) {
                 // the aligned dword holding the scale (it never crosses a page)
                 const uintptr_t sp = reinterpret_cast<uintptr_t>(srow[pb] + gg);
@@ -284,7 +294,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
                     sb + qa * NT * 16 + wave * 1024);
         }
     };
-    auto issue_all = [&](int gg, char *sb) {
+    auto issue_all = [&](int gg, uint32_t sb) {
         static_for<SH::NOPS>([&](auto Q) { dma_unit(Q, gg, sb); });
     };
 
@@ -417,10 +427,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
             for (int b = 0; b < NB; ++b)
                 acc[pb][b] = f32x16{};
 
-        issue_all(0, ring);
-        issue_all(min(1, G - 1), ring + SH::STAGE);
+        issue_all(0, ring_l);
+        issue_all(min(1, G - 1), ring_l + SH::STAGE);
         if constexpr (S > 3)
-            issue_all(min(2, G - 1), ring + 2 * SH::STAGE);
+            issue_all(min(2, G - 1), ring_l + 2 * SH::STAGE);
         // group 0's codes and scales (its activations and the later stages
         // may still be in flight); the barrier also publishes the codebooks
         // and the row factors
@@ -448,7 +458,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
             const int st_fill = (st == 0) ? S - 1 : st - 1;
             const char *sa = ring + st * SH::STAGE;
             const char *sn = ring + st_next * SH::STAGE;
-            char *sf = ring + st_fill * SH::STAGE;
+            const uint32_t sf = ring_l + st_fill * SH::STAGE;
             const int gf = min(g + S - 1, G - 1);
             const int gn = min(g + 1, G - 1);
             wait_vm<SH::NDMA_A + (S - 3) * SH::NOPS>();

@@ -132,8 +132,6 @@ struct GemmArgs {
     const int32_t *row_map[2];     // with one projection, [1] may hold gate's map (split SwiGLU)
     const uint16_t *codebook[2];
     int cb_bytes[2];
-    int cb_off[2];                 // LDS byte offsets of the codebooks
-    int kf_off;                    // LDS byte offset of the tile's row factors
     int rows, groups, wpr;
     const f16 *act;                // range-scaled fp16 activation rows
     int act_stride;                // halves between rows
@@ -163,10 +161,12 @@ struct GemmShape {
     static constexpr int STAGE = A_BYTES + NPB * WIN;
     // vector-memory operations per stage and wave: scales, code windows, activations
     static constexpr int NOPS = NDMA_A + NPB * (BWin<D, BITS>::NDMA + 1);
-    // LDS: the largest codebooks (64 KiB at most each) and the tile's row
-    // factors are dynamic, the ring static; four stages when they fit
+    // LDS, one static array from address 0: a slot per codebook of the
+    // largest size (64 KiB at most each), the tile's row factors, then the
+    // ring; four stages when they fit
     static constexpr int CB_MAX = ((1 << BITS) * D * 2 < 65536) ? (1 << BITS) * D * 2 : 65536;
-    static constexpr int FIXED = NPROJ * CB_MAX + 32 * MB * 4;
+    static constexpr int KF_OFF = NPROJ * CB_MAX;
+    static constexpr int FIXED = KF_OFF + 32 * MB * 4;   // a multiple of 16: the ring's offset
     static constexpr int S = (FIXED + 4 * STAGE <= kLdsBudget) ? 4 : 3;
     static constexpr bool FITS = FIXED + S * STAGE <= kLdsBudget;
 };
@@ -182,12 +182,15 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
     constexpr int NN = SH::NN;
     constexpr int NPB = SH::NPB;
     if constexpr (SH::FITS) {
-    // codebooks and row factors: dynamic LDS; the ring of S stages: static
-    extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-    char *const lb = reinterpret_cast<char *>(lds);
-    __shared__ __attribute__((aligned(16))) char ring[S * SH::STAGE];
+    // codebook slots and row factors, then the ring of S stages, in the
+    // kernel's only LDS array: the slots sit at fixed addresses, which the
+    // codebook reads carry as immediate offsets
+    __shared__ __attribute__((aligned(16))) char smem[SH::FIXED + S * SH::STAGE];
+    char *const lb = smem;
+    char *const ring = smem + SH::FIXED;
     const uint32_t lb_l = lds_addr(lb);     // LDS addresses of the two regions
     const uint32_t ring_l = lds_addr(ring);
+    auto cb_slot = [](int p) { return p == 0 ? 0 : SH::CB_MAX; };
 
     // Workgroup L runs on XCD L % 8 (round-robin dispatch); all weight-row
     // tiles of M tile t run on XCD t % 8 one after another, so the tile's
@@ -215,8 +218,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
 #pragma unroll
     for (int p = 0; p < NPROJ; ++p) {
         const char *src = reinterpret_cast<const char *>(a.codebook[p]);
-        char *dst = lb + a.cb_off[p];
-        const uint32_t dst_l = lb_l + (uint32_t)a.cb_off[p];
+        char *dst = lb + cb_slot(p);
+        const uint32_t dst_l = lb_l + (uint32_t)cb_slot(p);
         const int n16 = a.cb_bytes[p] >> 4;
         for (int i0 = 0; i0 < n16; i0 += NT)
             if (i0 + tid < n16)
@@ -224,7 +227,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
         for (int i = (n16 << 2) + tid; i < (a.cb_bytes[p] >> 2); i += NT)
             reinterpret_cast<uint32_t *>(dst)[i] = reinterpret_cast<const uint32_t *>(src)[i];
     }
-    float *kf = reinterpret_cast<float *>(lb + a.kf_off);
+    float *kf = reinterpret_cast<float *>(lb + SH::KF_OFF);
     for (int r = tid; r < 32 * MB; r += NT) {
         const int p = m0 + min(r, mlen - 1);
         const int row = a.perm ? a.perm[p] / a.act_div : p;
@@ -366,7 +369,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
     };
     // lookup: the codebook entries of slice j (unscaled)
     auto lookup = [&](int p, int j, const uint32_t (&nw)[NW], f16x8 &o) {
-        const uint32_t *cb = reinterpret_cast<const uint32_t *>(lb + a.cb_off[p]);
+        const uint32_t *cb = reinterpret_cast<const uint32_t *>(lb + cb_slot(p));
         constexpr uint32_t mask = (1u << BITS) - 1u;
         union { f16x8 v; uint32_t u[4]; } r;
 #pragma unroll
@@ -568,20 +571,6 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
 
 constexpr int kGemmWaves = 4;
 
-// Dynamic LDS of one launch: codebooks, row factors (the ring is static).
-template <int NPROJ, int MB>
-inline size_t gemm_layout(GemmArgs &a)
-{
-    size_t off = 0;
-    for (int p = 0; p < NPROJ; ++p) {
-        a.cb_off[p] = (int)off;
-        off += ((size_t)a.cb_bytes[p] + 15) & ~(size_t)15;
-    }
-    a.kf_off = (int)off;
-    off += (size_t)32 * MB * 4;
-    return off;
-}
-
 // hipErrorOutOfMemory: this geometry's codebooks leave no room for the ring
 // (the caller then splits gate and up into two launches).
 template <int D, int BITS, int NPROJ, int MB>
@@ -592,20 +581,13 @@ static hipError_t gemm_launch(GemmArgs a, int tile_cap, hipStream_t stream)
     if constexpr (!SH::FITS) {
         return hipErrorOutOfMemory;
     } else {
-        const size_t lds = gemm_layout<NPROJ, MB>(a);
         const void *kern = reinterpret_cast<const void *>(k_gemm<D, BITS, NPROJ, MB, WAVES>);
-        if (lds > 65536) {
-            hipError_t err = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)lds);
-            if (err != hipSuccess)
-                return err;
-        }
         a.n_ntiles = (a.rows + SH::WG_ROWS - 1) / SH::WG_ROWS;
         const int64_t wgs = (int64_t)((tile_cap + 7) / 8) * 8 * a.n_ntiles;
         if (wgs > 0x7fffffff)
             return hipErrorInvalidValue;
         void *args[] = {&a};
-        return hipLaunchKernel(kern, dim3((unsigned)wgs), dim3(64 * WAVES), args, lds, stream);
+        return hipLaunchKernel(kern, dim3((unsigned)wgs), dim3(64 * WAVES), args, 0, stream);
     }
 }
 

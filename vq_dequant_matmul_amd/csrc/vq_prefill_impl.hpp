@@ -171,6 +171,12 @@ struct GemmShape {
     static constexpr bool FITS = FIXED + S * STAGE <= kLdsBudget;
 };
 
+// The K step's interleave: after each MFMA, up to this many LDS reads and
+// VALU instructions (a sweep of 1-3 LDS reads and 2-4 VALU on the full-size
+// gate+up layers put two and three ahead, by about 1 %).
+constexpr int kSchedDs = 2;
+constexpr int kSchedValu = 3;
+
 template <int D, int BITS, int NPROJ, int MB, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
 {
@@ -510,13 +516,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
                     for (int pb = 0; pb < NPB; ++pb)
                         scale(bf[pb][j - 1], s2[pb]);
                 }
-                // interleave the side work with the MFMAs of this slice (a
-                // sweep of the pattern on full-size layers put two LDS reads
-                // and four VALU per MFMA a few percent ahead of one and three)
+                // interleave the side work with the MFMAs of this slice
                 static_for<NB * NPB>([&](auto) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // two LDS reads
-                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // four VALU
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, kSchedDs, 0);     // LDS reads
+                    __builtin_amdgcn_sched_group_barrier(0x002, kSchedValu, 0);   // VALU
                 });
                 __builtin_amdgcn_sched_barrier(0);
             });

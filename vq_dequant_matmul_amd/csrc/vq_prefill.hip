@@ -98,12 +98,10 @@ __device__ void build_tiles(const int *cnt, const int *offs, int *toff, int E, i
 }
 
 // Route grouping for the MoE FFN: pairs q = t*top_k + s by expert.
-__global__ __launch_bounds__(kRouteThreads) void k_route(const int32_t *__restrict__ ids, int P,
-                                                         int E, int mt, int32_t *__restrict__ offs,
-                                                         int32_t *__restrict__ perm,
-                                                         int32_t *__restrict__ pos,
-                                                         int32_t *__restrict__ tiles,
-                                                         int32_t *__restrict__ n_tiles)
+__device__ __forceinline__ void route_body(const int32_t *__restrict__ ids, int P, int E, int mt,
+                                           int32_t *__restrict__ offs, int32_t *__restrict__ perm,
+                                           int32_t *__restrict__ pos, int32_t *__restrict__ tiles,
+                                           int32_t *__restrict__ n_tiles)
 {
     extern __shared__ int s[];
     int *cnt = s, *base = s + E, *fill = s + 2 * E, *toff = s + 3 * E, *scratch = s + 4 * E;
@@ -181,11 +179,10 @@ __global__ __launch_bounds__(kRouteThreads) void k_tiles_from_offsets(
 // the rest again.
 constexpr int kRowRegs = 8;
 
-__global__ __launch_bounds__(256) void k_rowscale(const void *__restrict__ x, int f32, int rows,
-                                                  int cols, int64_t stride, f16 *__restrict__ out,
-                                                  int32_t *__restrict__ k)
+__device__ __forceinline__ void rowscale_row(const void *__restrict__ x, int f32, int rows,
+                                             int cols, int64_t stride, f16 *__restrict__ out,
+                                             int32_t *__restrict__ k, int row)
 {
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= rows)
         return;
@@ -252,6 +249,30 @@ __global__ __launch_bounds__(256) void k_rowscale(const void *__restrict__ x, in
         convert(*reinterpret_cast<const uint4 *>(p + (int64_t)c * esz), c);
     if (lane == 0)
         k[row] = ex;
+}
+
+__global__ __launch_bounds__(256) void k_rowscale(const void *__restrict__ x, int f32, int rows,
+                                                  int cols, int64_t stride, f16 *__restrict__ out,
+                                                  int32_t *__restrict__ k)
+{
+    rowscale_row(x, f32, rows, cols, stride, out, k, blockIdx.x * 4 + (threadIdx.x >> 6));
+}
+
+// The routing (workgroup 0) and the activation rows' scaling (the other
+// workgroups, kRouteThreads / 64 rows each) in one launch: they are
+// independent, and the routing alone leaves the rest of the chip idle.
+__global__ __launch_bounds__(kRouteThreads) void k_route_rowscale(
+    const int32_t *__restrict__ ids, int P, int E, int mt, int32_t *__restrict__ offs,
+    int32_t *__restrict__ perm, int32_t *__restrict__ pos, int32_t *__restrict__ tiles,
+    int32_t *__restrict__ n_tiles, const void *__restrict__ x, int f32, int rows, int cols,
+    f16 *__restrict__ out, int32_t *__restrict__ k)
+{
+    if (blockIdx.x == 0) {
+        route_body(ids, P, E, mt, offs, perm, pos, tiles, n_tiles);
+        return;
+    }
+    const int row = (blockIdx.x - 1) * (kRouteThreads / 64) + (threadIdx.x >> 6);
+    rowscale_row(x, f32, rows, cols, (int64_t)cols, out, k, row);
 }
 
 // y[t][c] = sum over slots s (in order) of w[t][s] * z[pos[t*k + s]][c].
@@ -510,16 +531,17 @@ hipError_t launch_moe_prefill(const TensorDev &g, const TensorDev &u, const Tens
     const int P = n_tok * top_k;
     const int E = g.n_experts;
 
+    // routing and the activation rows' scaling in one launch
     const size_t lds_r = (size_t)(4 * E + 17) * 4;
-    hipLaunchKernelGGL(k_route, dim3(1), dim3(kRouteThreads), lds_r, stream, ids, P, E,
-                       32 * w.mb, offs, perm, pos, tiles, n_tiles);
+    const int rs_wgs = (n_tok + kRouteThreads / 64 - 1) / (kRouteThreads / 64);
+    hipLaunchKernelGGL(k_route_rowscale, dim3((unsigned)(1 + rs_wgs)), dim3(kRouteThreads), lds_r,
+                       stream, ids, P, E, 32 * w.mb, offs, perm, pos, tiles, n_tiles, x, x_f32,
+                       n_tok, g.cols, xs, xk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     if (g.n_stored == 0 || u.n_stored == 0 || dn.n_stored == 0)
         return launch_zero(y, (int64_t)n_tok * dn.rows, stream);
-    if ((e = launch_rowscale(x, x_f32, n_tok, g.cols, xs, xk, stream)) != hipSuccess)
-        return e;
     const KernelEvents &ev = kernel_events();
     if (ev.start)
         (void)hipEventRecord(ev.start, stream);

@@ -5,16 +5,19 @@ A step is one pass of the routed SwiGLU expert FFN (``vq_moe_ffn``: route
 grouping, codebook staging, code unpacking, lookup-and-scale, the fused dot
 products or MFMA tiles, SwiGLU, the down projection and the gate-weighted
 combine) over one batch of synthetic input.  The default workload is the
-decode step of a 128-expert, top-8 layer (hidden 2048, expert inter 768)
-with every projection at d=4/K=512 (9-bit codes), one token per step;
-``--workload`` selects the other seeded layers (decode batches of 1 and 8
-tokens on a 512-expert top-10 layer; prefill of 2048 / 4096 tokens).
+largest one: prefill of 4096 tokens through a 512-expert, top-10 layer
+(hidden 4096, expert inter 1024) with every projection at d=2/K=256 (8-bit
+codes) and 12.43 % of the rows skip-zero; ``--workload`` selects the other
+seeded layers (decode of 1 token on a 128-expert top-8 layer at d=4/K=512,
+decode batches of 1 and 8 tokens on the 512-expert layer, prefill of 2048
+tokens on a 128-expert layer at d=4/K=2048).
 
 Inputs are resident in HBM before timing starts.  Each step uses fresh
-routes and activations, and steps rotate over several copies of the layer at
-distinct addresses so the weights come from HBM, not the 256 MB Infinity
-Cache.  The K timed steps are captured once in a HIP graph and replayed
-(a graph removes launch overhead only; every kernel runs).
+routes and activations, and steps rotate over enough copies of the layer at
+distinct addresses that a copy is used again only after four times the
+256 MB Infinity Cache of other steps' bytes, so the weights come from HBM.
+The K timed steps are captured once in a HIP graph and replayed (a graph
+removes launch overhead only; every kernel runs).
 
 Decode workloads report GB/s of algorithmic bytes (the routed experts'
 packed codes, scales and row maps, the codebooks, activations, outputs, ids
@@ -52,7 +55,8 @@ METRIC = "VQ MoE expert GB/s (decode, % HBM peak) and TFLOP/s (prefill, % MFMA p
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 MALL_BYTES = 256 << 20
-DEFAULT_WORKLOAD = "moe_decode_e128_h2048_i768_d4k512_b1"
+MAX_COPY_BYTES = 120 << 30     # device memory spent on layer copies at most
+DEFAULT_WORKLOAD = "moe_prefill_e512_h4096_i1024_d2k256_t4096_sz"
 CSRC = os.path.join(ROOT, "vq_dequant_matmul_amd", "csrc")
 TRAFFIC = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
 
@@ -140,6 +144,64 @@ def recorded_traffic(workload: str, family: str):
     return None
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def oracle_baseline(run, budget_s: float, max_samples: int, scale: float, unit: str,
+                    digits: int, what: str):
+    """Time the CPU oracle on samples run(j) (each returns its algorithmic
+    work) at all of the oracle's OpenMP threads until budget_s is spent, then
+    the same samples again at one thread (at most a third of the budget).
+    Returns the cpu_baseline record."""
+    import oracle
+    oracle.build(force=False)
+    cores = oracle.threads()
+    t_all, n, work = 0.0, 0, 0
+    while t_all < budget_s and n < max_samples:
+        c0 = time.perf_counter()
+        w = run(n)
+        t_all += time.perf_counter() - c0
+        work += w
+        n += 1
+    oracle.set_threads(1)
+    try:
+        t_one, n1, work1 = 0.0, 0, 0
+        while n1 < n and (n1 == 0 or t_one < budget_s / 3):
+            c0 = time.perf_counter()
+            w = run(n1)
+            t_one += time.perf_counter() - c0
+            work1 += w
+            n1 += 1
+    finally:
+        oracle.set_threads(cores)
+    log(f"[bench] cpu oracle: {n} samples in {t_all:.1f}s at {cores} threads, "
+        f"{n1} in {t_one:.1f}s at 1 thread")
+    return {"value": round(work / t_all / scale, digits), "unit": unit, "cores": cores,
+            "kind": "oracle", "sample": f"{n} x {what}, {t_all:.1f}s",
+            "cpu_model": cpu_model(),
+            "one_thread": {"value": round(work1 / t_one / scale, digits), "unit": unit,
+                           "cores": 1, "sample": f"{n1} x {what}, {t_one:.1f}s"}}
+
+
+def launch_stats(durs) -> dict:
+    """Mean, p10, p50 and p90 of per-launch durations (seconds) in us."""
+    import numpy as np
+    d = np.asarray(durs) * 1e6
+    return {"mean": round(float(d.mean()), 2), "p10": round(float(np.percentile(d, 10)), 2),
+            "p50": round(float(np.percentile(d, 50)), 2),
+            "p90": round(float(np.percentile(d, 90)), 2), "n": int(d.size)}
+
+
 def expert_bytes(T, e: int) -> int:
     """Stored bytes of one expert of one projection (codes, scales, row map)."""
     rows = T.expert_stored_rows(e)
@@ -184,43 +246,34 @@ def main():
     n_steps = K + W
 
     # ---- layer, copies, per-step inputs (all resident before timing) ---------------
+    # n_steps inputs for the timed steps, then n_k more for the dominant
+    # kernel's timing loop (every launch there has its own routes too)
     t0 = time.perf_counter()
     gate_h, up_h, down_h = synth.make_moe_layer(wl)
     layer_bytes = sum(t.stored_bytes() for t in (gate_h, up_h, down_h))
-    L = args.layers or max(2, math.ceil(4 * MALL_BYTES / layer_bytes))
-    base = [vq.VQTensor.from_host(t) for t in (gate_h, up_h, down_h)]
-    layers = [base] + [[t.clone() for t in base] for _ in range(L - 1)]
     xs, ids, ws = [], [], []
-    for i in range(n_steps):
+    for i in range(n_steps + n_k):
         x, r, w = synth.make_moe_inputs(wl, i)
         xs.append(x)
         ids.append(r)
         ws.append(w)
-    x_dev = torch.from_numpy(np.stack(xs).view(np.int16)).view(torch.bfloat16).cuda()
-    ids_dev = torch.from_numpy(np.stack(ids)).cuda()
-    w_dev = torch.from_numpy(np.stack(ws)).cuda()
-    y = torch.empty((wl.n_tok, wl.hidden), dtype=torch.float32, device="cuda")
-    ws_bytes = vq.vq_moe_ffn_workspace_size(*base, wl.n_tok, wl.top_k)
-    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-    torch.cuda.synchronize()
-    log(f"[bench] {args.workload}: {L} layer copies x {layer_bytes / 1e6:.1f} MB, "
-        f"{n_steps} step inputs, workspace {ws_bytes / 1e6:.1f} MB, "
-        f"setup {time.perf_counter() - t0:.1f}s")
 
     # ---- algorithmic work -------------------------------------------------------------
     cb_bytes = sum(t.K * t.d * 2 for t in (gate_h, up_h, down_h))
     io_bytes = wl.n_tok * wl.hidden * (2 + 4) + wl.n_tok * wl.top_k * 8
     live = {id(t): np.array([t.expert_stored_rows(e) for e in range(wl.n_experts)])
             for t in (gate_h, up_h, down_h)}
+    ebytes = {id(t): np.array([expert_bytes(t, e) for e in range(wl.n_experts)], dtype=np.int64)
+              for t in (gate_h, up_h, down_h)}
 
     def step_bytes(i):
         uniq = np.unique(ids[i])
-        return int(sum(expert_bytes(t, int(e)) for e in uniq for t in (gate_h, up_h, down_h))
+        return int(sum(ebytes[id(t)][uniq].sum() for t in (gate_h, up_h, down_h))
                    + cb_bytes + io_bytes)
 
     def gate_up_bytes(i):
         uniq = np.unique(ids[i])
-        return int(sum(expert_bytes(t, int(e)) for e in uniq for t in (gate_h, up_h))
+        return int(sum(ebytes[id(t)][uniq].sum() for t in (gate_h, up_h))
                    + gate_h.K * gate_h.d * 2 + up_h.K * up_h.d * 2
                    + wl.n_tok * wl.hidden * 2 + wl.n_tok * wl.top_k * (4 + 4 * wl.inter))
 
@@ -231,6 +284,28 @@ def main():
     def step_flops(i):
         r = ids[i].ravel()
         return gate_up_flops(i) + int(2 * wl.inter * live[id(down_h)][r].sum())
+
+    # Layer copies: step i uses copy i % L, so a copy (and every byte of it)
+    # is touched again only after L - 1 other steps; L makes those steps'
+    # bytes at least four times the Infinity Cache (the smallest step counts).
+    min_step = min(step_bytes(i) for i in range(n_steps + n_k))
+    L = args.layers or max(2, math.ceil(4 * MALL_BYTES / layer_bytes),
+                           1 + math.ceil(4 * MALL_BYTES / min_step))
+    if not args.layers and L * layer_bytes > MAX_COPY_BYTES:
+        L = max(2, MAX_COPY_BYTES // layer_bytes)
+        log(f"[bench] WARNING: layer copies capped at {L} ({L * layer_bytes / 1e9:.1f} GB)")
+    base = [vq.VQTensor.from_host(t) for t in (gate_h, up_h, down_h)]
+    layers = [base] + [[t.clone() for t in base] for _ in range(L - 1)]
+    x_dev = torch.from_numpy(np.stack(xs).view(np.int16)).view(torch.bfloat16).cuda()
+    ids_dev = torch.from_numpy(np.stack(ids)).cuda()
+    w_dev = torch.from_numpy(np.stack(ws)).cuda()
+    y = torch.empty((wl.n_tok, wl.hidden), dtype=torch.float32, device="cuda")
+    ws_bytes = vq.vq_moe_ffn_workspace_size(*base, wl.n_tok, wl.top_k)
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] {args.workload}: {L} layer copies x {layer_bytes / 1e6:.1f} MB, "
+        f"{n_steps} + {n_k} step inputs (smallest step {min_step / 1e6:.1f} MB), "
+        f"workspace {ws_bytes / 1e6:.1f} MB, setup {time.perf_counter() - t0:.1f}s")
 
     def step(i):
         G, U, D = layers[i % L]
@@ -282,22 +357,29 @@ def main():
     ms_per_step = elapsed * 1e3 / K
 
     # ---- dominant kernel: fused gate+up launch, HIP events on its stream -------------
-    # A queue of 256 MiB device copies keeps the GPU busy while the launches
-    # are queued, so the timed launches run back to back; the copy is also the
-    # kernel of known size the HBM byte counters are calibrated on.
+    # Launch j of the timing loop uses its own inputs (n_steps + j) and layer
+    # copy (n_steps + j) % L.  A queue of 256 MiB device copies keeps the GPU
+    # busy while the launches are queued, so the timed launches run back to
+    # back; the copy is also the kernel of known size the HBM byte counters
+    # are calibrated on.
+    kidx = [n_steps + j for j in range(n_k)]
     hip = HipEvents()
     src = torch.ones(1 << 26, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    for _ in range(48):
-        dst.copy_(src)
+
+    def queue_copies():
+        for _ in range(48):
+            dst.copy_(src)
+
+    queue_copies()
     if prefill:
         # ~1 ms launches: an event pair around each one (the library records
         # them on its launch stream around the gate+up GEMM only)
         pairs = [(hip.create(), hip.create()) for _ in range(n_k)]
-        for j in range(n_k):
+        for j, i in enumerate(kidx):
             vq.vq_set_kernel_events(pairs[j][0], pairs[j][1])
-            step(W + (j % K))
+            step(i)
         vq.vq_set_kernel_events(None, None)
         torch.cuda.synchronize()
         durs = np.array([hip.elapsed_ms(a, b) * 1e-3 for a, b in pairs])     # seconds
@@ -305,84 +387,93 @@ def main():
             hip.destroy(a)
             hip.destroy(b)
         k_mean = float(durs.mean())
+        stats = launch_stats(durs)
         timing = f"HIP event pair around each of {n_k} launches"
     else:
-        # ~10 us launches: per-launch event markers would add a few us each, so
+        # ~10 us launches: per-launch event markers add a few us each, so
         # one event pair spans n_k back-to-back launches of the gate+up stage
-        # alone (rotating layer copies and step inputs, as in the timed steps)
+        # alone for the mean; a second pass with a pair around each launch
+        # gives the spread (p10/p50/p90 include the markers' cost)
         h = torch.empty((wl.n_tok * wl.top_k, wl.inter), dtype=torch.float32, device="cuda")
-        ev0, ev1 = hip.create(), hip.create()
         stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        hip.record(ev0, stream)
-        for j in range(n_k):
-            i = W + (j % K)
+
+        def gate_up(i):
             G, U, _ = layers[i % L]
             vq.vq_moe_gate_up(G, U, x_dev[i], ids_dev[i], out=h)
+
+        ev0, ev1 = hip.create(), hip.create()
+        hip.record(ev0, stream)
+        for i in kidx:
+            gate_up(i)
         hip.record(ev1, stream)
         torch.cuda.synchronize()
         k_mean = hip.elapsed_ms(ev0, ev1) * 1e-3 / n_k
         hip.destroy(ev0)
         hip.destroy(ev1)
+        queue_copies()
+        pairs = [(hip.create(), hip.create()) for _ in range(n_k)]
+        for j, i in enumerate(kidx):
+            hip.record(pairs[j][0], stream)
+            gate_up(i)
+            hip.record(pairs[j][1], stream)
+        torch.cuda.synchronize()
+        durs = np.array([hip.elapsed_ms(a, b) * 1e-3 for a, b in pairs])
+        for a, b in pairs:
+            hip.destroy(a)
+            hip.destroy(b)
+        stats = launch_stats(durs)
         del h
-        timing = f"one HIP event pair around {n_k} back-to-back launches"
+        timing = (f"one HIP event pair around {n_k} back-to-back launches (mean); "
+                  f"a pair around each launch for the percentiles")
     del src, dst
     if prefill:
-        kwork = np.array([gate_up_flops(W + (j % K)) for j in range(n_k)])
+        kwork = np.array([gate_up_flops(i) for i in kidx])
         achieved = float(kwork.mean() / k_mean / 1e12)
         roofline = {"bound": "mfma", "achieved": round(achieved, 1),
                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4),
                     "traffic": recorded_traffic(args.workload, family),
                     "kernel": "vq::k_gemm (gate+up grouped GEMM, SwiGLU epilogue)",
-                    "launch_us": round(k_mean * 1e6, 2), "flops_per_launch": int(kwork.mean()),
-                    "timing": timing}
+                    "launch_us": round(k_mean * 1e6, 2), "launch_us_stats": stats,
+                    "flops_per_launch": int(kwork.mean()), "timing": timing}
     else:
-        kwork = np.array([gate_up_bytes(W + (j % K)) for j in range(n_k)])
+        kwork = np.array([gate_up_bytes(i) for i in kidx])
         achieved = float(kwork.mean() / k_mean / 1e9)
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": recorded_traffic(args.workload, family),
                     "kernel": "vq::k_rows (gate+up+SwiGLU, fused)",
-                    "launch_us": round(k_mean * 1e6, 2), "bytes_per_launch": int(kwork.mean()),
-                    "timing": timing}
-    log(f"[bench] dominant kernel: {k_mean * 1e6:.2f} us/launch, {achieved:.1f} {roofline['unit']}")
+                    "launch_us": round(k_mean * 1e6, 2), "launch_us_stats": stats,
+                    "bytes_per_launch": int(kwork.mean()), "timing": timing}
+    log(f"[bench] dominant kernel: {k_mean * 1e6:.2f} us/launch "
+        f"(p10 {stats['p10']}, p90 {stats['p90']}), {achieved:.1f} {roofline['unit']}")
 
     # ---- CPU oracle on a bounded sample ------------------------------------------------
     cpu = None
     if args.cpu_seconds > 0:
         import oracle
-        oracle.build(force=False)
-        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-        t_cpu, n_cpu, work = 0.0, 0, 0
         rng = np.random.default_rng(0)
-        while t_cpu < args.cpu_seconds and n_cpu < 10 * n_steps:
-            i = W + n_cpu % K
-            if prefill:
-                # a few tokens of the step: each token's output is independent
-                toks = np.sort(rng.choice(wl.n_tok, size=2, replace=False)).astype(np.int32)
-                c0 = time.perf_counter()
-                oracle.moe_ffn(gate_h, up_h, down_h, xs[i], ids[i], ws[i], tokens=toks)
-                t_cpu += time.perf_counter() - c0
-                r = ids[i][toks].ravel()
-                work += int(2 * wl.hidden * (live[id(gate_h)][r].sum() + live[id(up_h)][r].sum())
-                            + 2 * wl.inter * live[id(down_h)][r].sum())
-            else:
-                c0 = time.perf_counter()
-                oracle.moe_ffn(gate_h, up_h, down_h, xs[i], ids[i], ws[i])
-                t_cpu += time.perf_counter() - c0
-                work += step_bytes(i)
-            n_cpu += 1
         if prefill:
-            cpu = {"value": round(work / t_cpu / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-                   "kind": "oracle",
-                   "sample": f"{n_cpu} x 2 sampled tokens of the same workload "
-                             f"({wl.top_k} routed experts each), {t_cpu:.1f}s"}
+            # a few tokens of a step: each token's output is independent
+            toks = [np.sort(rng.choice(wl.n_tok, size=2, replace=False)).astype(np.int32)
+                    for _ in range(10 * n_steps)]
+
+            def run(j):
+                i = W + j % K
+                oracle.moe_ffn(gate_h, up_h, down_h, xs[i], ids[i], ws[i], tokens=toks[j])
+                r = ids[i][toks[j]].ravel()
+                return int(2 * wl.hidden * (live[id(gate_h)][r].sum() + live[id(up_h)][r].sum())
+                           + 2 * wl.inter * live[id(down_h)][r].sum())
+            cpu = oracle_baseline(run, args.cpu_seconds, 10 * n_steps, 1e12, "TFLOP/s", 6,
+                                  f"2 sampled tokens of a step ({wl.top_k} routed experts each)")
         else:
-            cpu = {"value": round(work / t_cpu / 1e9, 4), "unit": "GB/s", "cores": cores,
-                   "kind": "oracle",
-                   "sample": f"{n_cpu} decode steps of the same workload ({wl.n_tok} token(s), "
-                             f"{wl.top_k} routed experts each), {t_cpu:.1f}s"}
-        log(f"[bench] cpu oracle: {n_cpu} samples in {t_cpu:.1f}s")
+            def run(j):
+                i = W + j % K
+                oracle.moe_ffn(gate_h, up_h, down_h, xs[i], ids[i], ws[i])
+                return step_bytes(i)
+            cpu = oracle_baseline(run, args.cpu_seconds, 10 * n_steps, 1e9, "GB/s", 4,
+                                  f"whole decode steps ({wl.n_tok} token(s), "
+                                  f"{wl.top_k} routed experts each)")
 
     rec = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": K,
@@ -544,22 +635,14 @@ def bench_stack(args, sw):
     cpu = None
     if args.cpu_seconds > 0:
         import oracle
-        oracle.build(force=False)
-        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-        t_cpu, n_cpu, work = 0.0, 0, 0
-        while t_cpu < args.cpu_seconds and n_cpu < K:
-            i = W + n_cpu
+
+        def run(j):
+            i = W + j % K
             layers = [(*hl[sw.layer_bits(l)], ids[i][l], ws[i][l]) for l in range(sw.n_layers)]
-            c0 = time.perf_counter()
             oracle.moe_stack(layers, xs[i])
-            t_cpu += time.perf_counter() - c0
-            work += step_bytes(i)
-            n_cpu += 1
-        cpu = {"value": round(work / t_cpu / 1e9, 4), "unit": "GB/s", "cores": cores,
-               "kind": "oracle",
-               "sample": f"{n_cpu} whole steps of the same workload ({sw.n_layers} layers), "
-                         f"{t_cpu:.1f}s"}
-        log(f"[bench] cpu oracle: {n_cpu} steps in {t_cpu:.1f}s")
+            return step_bytes(i)
+        cpu = oracle_baseline(run, args.cpu_seconds, K, 1e9, "GB/s", 4,
+                              f"whole steps of the same workload ({sw.n_layers} layers)")
 
     rec = {
         "metric": "VQ MoE layer stack GB/s (decode, % HBM peak)", "value": round(value, 2),
@@ -663,26 +746,19 @@ def bench_fit(args, fw):
     cpu = None
     if args.cpu_seconds > 0:
         import oracle
-        oracle.build(force=False)
-        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
         # a bounded slice: the first rows of the tensor with a proportional
         # share of the fit set (its indices that fall in those rows)
         rows = 1024
         n_sub = fw.cols // fw.d
         sub_s = sample[sample < rows * n_sub]
         sub_i = init % (rows * n_sub)
-        t_cpu, n_cpu, work = 0.0, 0, 0
-        while t_cpu < args.cpu_seconds and n_cpu < 1000:
-            c0 = time.perf_counter()
+
+        def run(j):
             oracle.fit(w[:rows], fw.d, fw.bits, fw.K, sub_s, sub_i, fw.iters)
-            t_cpu += time.perf_counter() - c0
-            work += (fw.iters * len(sub_s) + rows * n_sub) * fw.K * fw.d * 3
-            n_cpu += 1
-        cpu = {"value": round(work / t_cpu / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-               "kind": "oracle",
-               "sample": f"{n_cpu} fits of the first {rows} rows with their share of the fit "
-                         f"set ({len(sub_s)} subvectors), {t_cpu:.1f}s"}
-        log(f"[bench] cpu oracle: {n_cpu} fits in {t_cpu:.1f}s")
+            return (fw.iters * len(sub_s) + rows * n_sub) * fw.K * fw.d * 3
+        cpu = oracle_baseline(run, args.cpu_seconds, 1000, 1e12, "TFLOP/s", 6,
+                              f"fits of the first {rows} rows with their share of the fit "
+                              f"set ({len(sub_s)} subvectors)")
 
     rec = {
         "metric": "VQ codebook fit TFLOP/s (nearest-entry searches, % fp32 VALU peak)",
@@ -806,19 +882,12 @@ def bench_gather(args, wl):
     cpu = None
     if args.cpu_seconds > 0:
         import oracle
-        oracle.build(force=False)
-        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-        t_cpu, n_cpu = 0.0, 0
-        while t_cpu < args.cpu_seconds and n_cpu < 10 * n_steps:
-            c0 = time.perf_counter()
-            oracle.gather(T, ids[W + n_cpu % K])
-            t_cpu += time.perf_counter() - c0
-            n_cpu += 1
-        cpu = {"value": round(n_cpu * step_bytes / t_cpu / 1e9, 4), "unit": "GB/s",
-               "cores": cores, "kind": "oracle",
-               "sample": f"{n_cpu} whole steps of the same workload ({wl.n_ids} rows each), "
-                         f"{t_cpu:.1f}s"}
-        log(f"[bench] cpu oracle: {n_cpu} steps in {t_cpu:.1f}s")
+
+        def run(j):
+            oracle.gather(T, ids[W + j % K])
+            return step_bytes
+        cpu = oracle_baseline(run, args.cpu_seconds, 10 * n_steps, 1e9, "GB/s", 4,
+                              f"whole steps of the same workload ({wl.n_ids} rows each)")
 
     rec = {
         "metric": "VQ embedding row gather GB/s (% HBM peak)", "value": round(value, 2),

@@ -36,8 +36,10 @@
  *     (vq_last_error).  Device-resident contents (codes >= K, row-map
  *     entries, expert ids out of range, non-finite values) cannot be checked
  *     without a synchronization and are preconditions: violating them gives
- *     undefined output but never an out-of-bounds access for codes (the code
- *     is masked to bits) -- ids and row maps must be in range.
+ *     undefined output but never an out-of-bounds access for codes (the
+ *     kernels' codebook lookups stay inside the LDS copy of the codebook, and
+ *     the exact dequantisation reads entry K-1 for a code >= K) -- ids and
+ *     row maps must be in range.
  *   - A HIP launch error returns VQ_ERR_HIP with the runtime's message.
  *   - Results are bit-reproducible run to run (no floating-point atomics).
  *   - One codebook per tensor, shared by all its experts: codebooks are

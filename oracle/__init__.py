@@ -104,6 +104,10 @@ def _load():
         lib.vqo_encode.argtypes = [I64, I32, I32, I32, I32, P, P, P, P]
         lib.vqo_fit.restype = ctypes.c_int
         lib.vqo_fit.argtypes = [I64, I32, I32, I32, I32, P, I64, P, P, I32, P, P, P]
+        lib.vqo_set_threads.restype = None
+        lib.vqo_set_threads.argtypes = [ctypes.c_int32]
+        lib.vqo_threads.restype = ctypes.c_int32
+        lib.vqo_threads.argtypes = []
         lib.vqo_swiglu.restype = ctypes.c_double
         lib.vqo_swiglu.argtypes = [ctypes.c_double, ctypes.c_double]
         _lib = lib
@@ -310,3 +314,13 @@ def fit(w: np.ndarray, d: int, bits: int, K: int, sample, init, iters: int):
 
 def swiglu(g: float, u: float) -> float:
     return _load().vqo_swiglu(g, u)
+
+
+def set_threads(n: int) -> None:
+    """OpenMP threads of the oracle's row loops (timing only; results do
+    not depend on it)."""
+    _load().vqo_set_threads(int(n))
+
+
+def threads() -> int:
+    return int(_load().vqo_threads())

@@ -14,6 +14,31 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads of the OpenMP loops below (they only split independent output
+   rows; no sum depends on the count).  Used to time the oracle at one
+   thread and at all host cores. */
+void vqo_set_threads(int32_t n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+int32_t vqo_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ---------------------------------------------------------------------- */
 /* Number formats                                                          */

@@ -138,6 +138,10 @@ int vqo_fit(int64_t n_rows, int32_t cols, int32_t d, int32_t bits, int32_t K, co
             int64_t n_sample, const int64_t *sample, const int64_t *init, int32_t iters,
             uint16_t *codebook, uint16_t *scales, uint32_t *codes);
 
+/* OpenMP threads of the loops above (n > 0), and the current count. */
+void vqo_set_threads(int32_t n);
+int32_t vqo_threads(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -165,3 +165,25 @@ def test_fit_argument_errors(lib):
         st = call(**kw)
         assert st == status, (kw, st)
         assert needle in lib.vq_last_error().decode(), (kw, lib.vq_last_error())
+
+
+def test_prefill_size_limits(lib):
+    """The grouped-GEMM path indexes its activation matrices (x rows, then
+    one h row per routed pair) in 32-bit bytes and counts routed pairs in
+    int32: sizes past either limit are refused before any GPU work."""
+    g = _t(rows=2048, cols=8192, n_experts=16, n_stored=16 * 2048)
+    u = _t(rows=2048, cols=8192, n_experts=16, n_stored=16 * 2048)
+    dn = _t(rows=8192, cols=2048, n_experts=16, n_stored=16 * 8192)
+    # 131072 tokens x top-8 x inter 2048 fp16 = 4 GiB of h
+    args = (ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn))
+    assert lib.vq_moe_ffn_workspace_size(*args, 131072, 8) == 0
+    st = lib.vq_moe_ffn(*args, 131072, 8, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == 2 and "limit" in lib.vq_last_error().decode()
+    # just below: accepted by the size check (then the workspace check fails)
+    assert lib.vq_moe_ffn_workspace_size(*args, 131071, 8) > 0
+    st = lib.vq_moe_ffn(*args, 131071, 8, FAKE, 1, FAKE, FAKE, FAKE, FAKE, 1, None)
+    assert st == 3 and "workspace" in lib.vq_last_error().decode()
+    # x itself: 262144 rows x 8192 columns of fp16 = 4 GiB
+    w = _t(rows=64, cols=8192, n_experts=2, n_stored=128)
+    st = lib.vq_expert_gemm(ctypes.byref(w), 262144, FAKE, 1, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == 2 and "limit" in lib.vq_last_error().decode()

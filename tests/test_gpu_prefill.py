@@ -105,6 +105,75 @@ def test_moe_prefill_full_size_sampled(name, n_sample):
     check_close(y[tokens], ref, name)
 
 
+def _cover_tokens(ids, E, experts, seed):
+    """Every token routed to one of `experts` (each such expert's whole block
+    of rows, so all of its M tiles), plus a greedy choice of further tokens
+    until every routed expert is covered by at least one token."""
+    sel = set(np.nonzero(np.isin(ids, list(experts)).any(axis=1))[0].tolist())
+    covered = set(np.unique(ids[sorted(sel)]).tolist()) if sel else set()
+    want = set(np.unique(ids).tolist())
+    rng = np.random.default_rng(seed)
+    for t in rng.permutation(ids.shape[0]):
+        if covered >= want:
+            break
+        new = set(ids[t].tolist()) - covered
+        if new:
+            sel.add(int(t))
+            covered |= new
+    assert covered >= want
+    return np.array(sorted(sel), dtype=np.int32)
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("name", [
+    "moe_prefill_e128_h2816_i704_d4k2048_t2048",
+    "moe_prefill_e512_h4096_i1024_d2k256_t4096_sz",
+])
+def test_moe_prefill_full_size_tiles(name):
+    """The full-size layers in the benchmarked launch configuration: all
+    tokens of the largest, the smallest and a median expert block (every M
+    tile of those experts, including remainder tiles), plus tokens covering
+    every routed expert, against the oracle."""
+    wl = synth.WORKLOADS[name]
+    gate, up, down = synth.make_moe_layer(wl)
+    x, ids, w = synth.make_moe_inputs(wl, 0)
+    y = _run_moe(gate, up, down, x, ids, w)
+    assert np.all(np.isfinite(y))
+    counts = np.bincount(ids.ravel(), minlength=wl.n_experts)
+    order = np.argsort(counts, kind="stable")
+    live = order[counts[order] > 0]
+    experts = {int(live[-1]), int(live[0]), int(live[len(live) // 2])}
+    tokens = _cover_tokens(ids, wl.n_experts, experts, 7)
+    ref = oracle.moe_ffn(gate, up, down, x, ids, w, tokens=tokens)
+    check_close(y[tokens], ref, f"{name} ({len(tokens)} tokens)")
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", [
+    "moe_prefill_e128_h2816_i704_d4k2048_t2048",
+    "moe_prefill_e512_h4096_i1024_d2k256_t4096_sz",
+])
+@pytest.mark.parametrize("proj", [0, 2])
+def test_expert_gemm_full_size(name, proj):
+    """vq_expert_gemm on a full-size projection with the workload's routed
+    block sizes; the largest, smallest and a median block are checked."""
+    wl = synth.WORKLOADS[name]
+    T = synth.make_moe_layer(wl)[proj]
+    _, ids, _ = synth.make_moe_inputs(wl, 0)
+    counts = np.bincount(ids.ravel(), minlength=wl.n_experts)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x = synth.make_x(wl.seed, 77 + proj, int(offs[-1]), T.cols, "bf16")
+    y = vq.vq_expert_gemm(_dev(T), x_to_torch(x), torch.from_numpy(offs).cuda()).cpu().numpy()
+    assert np.all(np.isfinite(y))
+    order = np.argsort(counts, kind="stable")
+    for e in {int(order[-1]), int(order[0]), int(order[len(order) // 2])}:
+        lo, hi = offs[e], offs[e + 1]
+        if lo == hi:
+            continue
+        check_close(y[lo:hi], oracle.linear(T, e, x[lo:hi]), f"{name} proj {proj} expert {e}")
+        assert np.all(y[lo:hi][:, dead_rows(T, e)].view(np.uint32) == 0)
+
+
 def test_moe_prefill_deterministic():
     E, k, H, I, T = 16, 4, 512, 256, 128
     gate = synth.make_tensor(90, 1, rows=I, cols=H, d=4, bits=9, n_experts=E)

@@ -388,6 +388,10 @@ VQ_EXPORT vq_status vq_expert_gemm(const vq_tensor *W, int32_t n_x_rows, const v
         return fail(VQ_ERR_INVALID_ARGUMENT, "y: must be a non-NULL, 16-byte aligned device pointer");
     if (!expert_offsets)
         return fail(VQ_ERR_INVALID_ARGUMENT, "expert_offsets: must be non-NULL");
+    if ((int64_t)n_x_rows * W->cols * 2 >= vq::kMaxGemmActBytes)
+        return fail(VQ_ERR_UNSUPPORTED,
+                    "x of %d x %d fp16 values reaches %lld bytes, the grouped GEMM's limit",
+                    n_x_rows, W->cols, (long long)vq::kMaxGemmActBytes);
     const vq::TensorDev td = vq::to_dev(*W);
     const size_t need = vq::gemm_workspace_bytes(td, n_x_rows);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
@@ -490,6 +494,24 @@ static vq_status check_ffn(const vq_tensor *gate, const vq_tensor *up, const vq_
     return VQ_OK;
 }
 
+// Size limits of the grouped-GEMM path: routed pairs are counted in int32,
+// and every activation matrix the GEMM reads (x rows, then one h row per
+// routed pair) is indexed in 32-bit bytes.
+static vq_status check_prefill_sizes(const vq_tensor &gate, int32_t n_tokens, int32_t top_k)
+{
+    const int64_t pairs = (int64_t)n_tokens * top_k;
+    if (pairs > vq::kMaxPrefillPairs)
+        return fail(VQ_ERR_UNSUPPORTED, "n_tokens * top_k = %lld exceeds %lld routed pairs",
+                    (long long)pairs, (long long)vq::kMaxPrefillPairs);
+    if ((int64_t)n_tokens * gate.cols * 2 >= vq::kMaxGemmActBytes ||
+        pairs * gate.rows * 2 >= vq::kMaxGemmActBytes)
+        return fail(VQ_ERR_UNSUPPORTED,
+                    "activations of %lld x %d or h of %lld x %d fp16 values reach %lld bytes, "
+                    "the grouped GEMM's limit", (long long)n_tokens, gate.cols, (long long)pairs,
+                    gate.rows, (long long)vq::kMaxGemmActBytes);
+    return VQ_OK;
+}
+
 // The small-batch FFN: gate+up+SwiGLU -> down -> slot-ordered combine, into y
 // (accumulate: added to y).  Sizes and the workspace are checked by the caller.
 static vq_status run_decode_ffn(const vq::TensorDev &g, const vq::TensorDev &u,
@@ -522,6 +544,8 @@ VQ_EXPORT size_t vq_moe_ffn_workspace_size(const vq_tensor *gate, const vq_tenso
         return 0;
     if (n_tokens <= kDecodeMaxTokens)
         return decode_ws(*gate, *down, n_tokens, top_k).total;
+    if (check_prefill_sizes(*gate, n_tokens, top_k) != VQ_OK)
+        return 0;
     return vq::moe_prefill_workspace_bytes(vq::to_dev(*gate), vq::to_dev(*up), vq::to_dev(*down),
                                            n_tokens, top_k);
 }
@@ -548,6 +572,8 @@ VQ_EXPORT vq_status vq_moe_ffn(const vq_tensor *gate, const vq_tensor *up, const
     const vq::TensorDev g = vq::to_dev(*gate), u = vq::to_dev(*up), dn = vq::to_dev(*down);
 
     if (n_tokens > kDecodeMaxTokens) {
+        if ((st = check_prefill_sizes(*gate, n_tokens, top_k)) != VQ_OK)
+            return st;
         const size_t need = vq::moe_prefill_workspace_bytes(g, u, dn, n_tokens, top_k);
         if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
             return fail(VQ_ERR_WORKSPACE,

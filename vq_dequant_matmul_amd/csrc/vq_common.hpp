@@ -156,14 +156,17 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h)
 
 // Power-of-two range scale for a block of activations: returns k such that
 // max|x| * 2^k lies in [2^14, 2^15), so every scaled value is an fp16 normal
-// (bf16 values then convert exactly); 0 for an all-zero block.
+// (bf16 values then convert exactly); 0 for an all-zero block.  k is at most
+// 126, so 2^k and 2^-k are both normal fp32 numbers: a block whose largest
+// magnitude is below 2^-111 is scaled by 2^126 only (its small values then
+// round in fp16 as subnormals instead of overflowing the scale).
 __device__ __forceinline__ int range_exponent(float amax)
 {
     if (!(amax > 0.0f))
         return 0;
     int ex;
     (void)frexpf(amax, &ex);   // amax = f * 2^ex, f in [0.5, 1)
-    return 15 - ex;
+    return min(15 - ex, 126);
 }
 
 __device__ __forceinline__ f16x2 pack_f16x2(float a, float b)

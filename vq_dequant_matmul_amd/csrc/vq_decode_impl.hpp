@@ -660,7 +660,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint32_t *__restrict__
                                                     const uint16_t *__restrict__ scales,
                                                     const uint16_t *__restrict__ codebook,
                                                     const int32_t *__restrict__ row_map, int rows,
-                                                    int groups, int wpr, int e,
+                                                    int groups, int wpr, int e, uint32_t kmax,
                                                     float *__restrict__ w)
 {
     using GM = Geom<D, BITS>;
@@ -682,7 +682,9 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint32_t *__restrict__
     const float sc = half_bits_to_float(scales[s * groups + g]);
 #pragma unroll
     for (int t = 0; t < GM::G; ++t) {
-        const uint32_t code = extract<BITS, GM::NW>(nw, t);
+        // a code >= K (a precondition violation) reads entry K-1, never past
+        // the codebook
+        const uint32_t code = min(extract<BITS, GM::NW>(nw, t), kmax);
 #pragma unroll
         for (int k = 0; k < D; ++k)
             out[t * D + k] = sc * half_bits_to_float(codebook[(int64_t)code * D + k]);
@@ -698,7 +700,8 @@ static hipError_t dequantize_db(const TensorDev &t, int e, float *w, hipStream_t
     const int64_t n = (int64_t)t.rows * t.groups;
     const int blocks = (int)((n + 255) / 256);
     hipLaunchKernelGGL((k_dequantize<D, BITS>), dim3(blocks), dim3(256), 0, stream, t.codes,
-                       t.scales, t.codebook, t.row_map, t.rows, t.groups, t.wpr, e, w);
+                       t.scales, t.codebook, t.row_map, t.rows, t.groups, t.wpr, e,
+                       (uint32_t)(t.K - 1), w);
     return hipGetLastError();
 }
 

@@ -113,4 +113,9 @@ constexpr int kMaxSlots = 1024;      // n_tokens * top_k in one routed launch
 constexpr int kMaxGroupsDecode = 128; // cols <= 8192
 constexpr int kMaxCodebookBytes = 65536;
 
+// Limits of the grouped-GEMM path (routed pairs are int32; activation
+// matrices are addressed in 32-bit bytes).
+constexpr int64_t kMaxPrefillPairs = 0x7fffffff;
+constexpr int64_t kMaxGemmActBytes = (int64_t)1 << 32;
+
 }  // namespace vq

@@ -165,6 +165,26 @@ vq_status vq_moe_ffn(const vq_tensor *gate, const vq_tensor *up, const vq_tensor
                      const int32_t *topk_ids, const float *topk_weights, float *y,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* vq_moe_ffn for callers that cannot allocate device memory (code under HIP
+   graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+   same computation and kernels as vq_moe_ffn, bit for bit, with the
+   workspace taken from a static device array of VQ_NOALLOC_SCRATCH_BYTES
+   (64 MiB) that every GPU the library runs on holds from the library's load
+   until the process ends.  Nothing is allocated or freed in the call.  A
+   call whose vq_moe_ffn_workspace_size() exceeds the array returns
+   VQ_ERR_UNSUPPORTED (that covers every decode batch up to 16 tokens x
+   1024 routed pairs of hidden + inter <= 16384, and prefill batches of a few
+   hundred routed pairs).  All calls on one GPU share its array: calls that
+   overlap on that GPU (several streams or threads at once) race and give
+   undefined output; calls in order on one stream are safe.  The array's
+   address is looked up on the first call on each device (with that device
+   current); `stream` must belong to the current device. */
+#define VQ_NOALLOC_SCRATCH_BYTES (64u << 20)
+vq_status vq_moe_ffn_noalloc(const vq_tensor *gate, const vq_tensor *up, const vq_tensor *down,
+                             int32_t n_tokens, int32_t top_k, const void *x, vq_dtype x_dtype,
+                             const int32_t *topk_ids, const float *topk_weights, float *y,
+                             void *stream);
+
 /* ---- the three stages of the small-batch FFN, callable one by one -------- */
 
 /* Stage 1 (gate, up, SwiGLU): for pair q = t*top_k + s with e = topk_ids[t][s],

@@ -187,3 +187,18 @@ def test_prefill_size_limits(lib):
     w = _t(rows=64, cols=8192, n_experts=2, n_stored=128)
     st = lib.vq_expert_gemm(ctypes.byref(w), 262144, FAKE, 1, FAKE, FAKE, FAKE, 1 << 40, None)
     assert st == 2 and "limit" in lib.vq_last_error().decode()
+
+
+def test_noalloc_refuses_batches_beyond_its_array(lib):
+    """vq_moe_ffn_noalloc takes its workspace from a 64 MiB static device
+    array: a batch that needs more is refused before any GPU work."""
+    g = _t(rows=1024, cols=4096, n_experts=64, n_stored=64 * 1024)
+    u = _t(rows=1024, cols=4096, n_experts=64, n_stored=64 * 1024)
+    dn = _t(rows=4096, cols=1024, n_experts=64, n_stored=64 * 4096)
+    args = (ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn))
+    assert lib.vq_moe_ffn_workspace_size(*args, 2048, 8) > 64 << 20
+    st = lib.vq_moe_ffn_noalloc(*args, 2048, 8, FAKE, 1, FAKE, FAKE, FAKE, None)
+    assert st == 2 and "static scratch array" in lib.vq_last_error().decode()
+    # argument errors come first, as in vq_moe_ffn
+    st = lib.vq_moe_ffn_noalloc(*args, 2048, 65, FAKE, 1, FAKE, FAKE, FAKE, None)
+    assert st == 1 and "top_k" in lib.vq_last_error().decode()

@@ -83,6 +83,7 @@ def load_library():
         "vq_expert_gemm": (ctypes.c_int, [T, I32, P, ctypes.c_int, P, P, P, SZ, P]),
         "vq_moe_ffn_workspace_size": (SZ, [T, T, T, I32, I32]),
         "vq_moe_ffn": (ctypes.c_int, [T, T, T, I32, I32, P, ctypes.c_int, P, P, P, P, SZ, P]),
+        "vq_moe_ffn_noalloc": (ctypes.c_int, [T, T, T, I32, I32, P, ctypes.c_int, P, P, P, P]),
         "vq_moe_gate_up": (ctypes.c_int, [T, T, I32, I32, P, ctypes.c_int, P, P, P]),
         "vq_moe_down": (ctypes.c_int, [T, I32, I32, P, P, P, P]),
         "vq_moe_combine": (ctypes.c_int, [I32, I32, I32, P, P, P, P]),
@@ -322,6 +323,24 @@ def vq_moe_ffn(gate: VQTensor, up: VQTensor, down: VQTensor, x: torch.Tensor,
     return out
 
 
+def vq_moe_ffn_noalloc(gate: VQTensor, up: VQTensor, down: VQTensor, x: torch.Tensor,
+                       topk_ids: torch.Tensor, topk_weights: torch.Tensor,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """vq_moe_ffn with its workspace in the library's static device array
+    (no workspace argument; raises VQError for batches that need more)."""
+    _require_gpu()
+    lib = load_library()
+    x = x.contiguous()
+    n, k = topk_ids.shape
+    if out is None:
+        out = torch.empty((n, gate.cols), dtype=torch.float32, device=x.device)
+    g, u, dn = gate.c(), up.c(), down.c()
+    _check(lib.vq_moe_ffn_noalloc(ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), n, k,
+                                  _ptr(x), _x_dtype(x), _ptr(topk_ids.contiguous()),
+                                  _ptr(topk_weights.contiguous()), _ptr(out), _stream()))
+    return out
+
+
 class _StackArgs:
     """The C layer array and the descriptors it points at, kept alive together."""
 
@@ -416,7 +435,7 @@ __all__ = [
     "VQError", "VQTensor", "build", "load_library", "vq_validate", "vq_dequantize",
     "vq_row_gather", "vq_fit",
     "vq_expert_gemv", "vq_expert_gemm", "vq_expert_gemm_workspace_size", "vq_moe_ffn",
-    "vq_moe_ffn_workspace_size", "vq_moe_gate_up", "vq_moe_down", "vq_moe_combine",
+    "vq_moe_ffn_workspace_size", "vq_moe_ffn_noalloc", "vq_moe_gate_up", "vq_moe_down", "vq_moe_combine",
     "vq_set_kernel_events", "vq_moe_stack", "vq_moe_stack_workspace_size",
     "VQ_F32", "VQ_BF16",
 ]

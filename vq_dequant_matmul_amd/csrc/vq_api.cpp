@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/vq.h"
@@ -596,6 +597,71 @@ VQ_EXPORT vq_status vq_moe_ffn(const vq_tensor *gate, const vq_tensor *up, const
                     workspace_bytes, workspace);
     return run_decode_ffn(g, u, dn, n_tokens, top_k, x, x_dtype == VQ_F32, topk_ids,
                           topk_weights, y, false, ws, workspace, s, "vq_moe_ffn (decode)");
+}
+
+// ------------------------------------------------------------------------------------
+// the routed FFN without allocation: its workspace is a static device array
+// ------------------------------------------------------------------------------------
+
+// One copy per GPU, created with the code object and held until the process
+// ends.  Host code never passes `scratch` itself to a kernel or a copy (on the
+// host the name is only a stand-in): it uses the address looked up below.
+static __device__ __align__(256) unsigned char scratch[VQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];   // device address of each GPU's `scratch` (null: not yet)
+
+// This GPU's address of `scratch`, looked up on the first call with the
+// device current and kept per device.
+hipError_t scratch_address(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+VQ_EXPORT vq_status vq_moe_ffn_noalloc(const vq_tensor *gate, const vq_tensor *up,
+                                       const vq_tensor *down, int32_t n_tokens, int32_t top_k,
+                                       const void *x, vq_dtype x_dtype, const int32_t *topk_ids,
+                                       const float *topk_weights, float *y, void *stream)
+{
+    vq_status st = check_ffn(gate, up, down, n_tokens, top_k);
+    if (st != VQ_OK)
+        return st;
+    if (n_tokens == 0)
+        return ok();
+    if (n_tokens > kDecodeMaxTokens && (st = check_prefill_sizes(*gate, n_tokens, top_k)) != VQ_OK)
+        return st;
+    const size_t need = vq_moe_ffn_workspace_size(gate, up, down, n_tokens, top_k);
+    if (need > (size_t)VQ_NOALLOC_SCRATCH_BYTES)
+        return fail(VQ_ERR_UNSUPPORTED,
+                    "vq_moe_ffn_noalloc: %d tokens x top-%d need %zu bytes of workspace; the "
+                    "static scratch array holds %zu (call vq_moe_ffn with a workspace instead)",
+                    n_tokens, top_k, need, (size_t)VQ_NOALLOC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess)
+        return hip_fail(e, "vq_moe_ffn_noalloc: address of the scratch array");
+    return vq_moe_ffn(gate, up, down, n_tokens, top_k, x, x_dtype, topk_ids, topk_weights, y, ws,
+                      (size_t)VQ_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // ------------------------------------------------------------------------------------

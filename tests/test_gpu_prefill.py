@@ -33,6 +33,8 @@ GEMM_CASES = [
     (2, 10, 96, 1024, 5, [0, 0, 40, 0, 9], "bf16", 0),
     (8, 12, 64, 256, 2, [33, 31], "bf16", 0),
     (4, 13, 130, 384, 2, [17, 60], "bf16", 3),
+    (2, 8, 300, 448, 3, [40, 100, 5], "bf16", 9),          # 8-bit, 7 groups a row
+    (2, 8, 520, 256, 2, [64, 97], "f32", 3),               # 8-bit, 4 groups, ragged rows
 ]
 
 
@@ -77,6 +79,7 @@ def _run_moe(gate, up, down, x, ids, w):
     (200, 16, 4, 384, 320, 4, 11, 0, "f32"),    # fp32 activations
     (96, 4, 4, 256, 128, 2, 10, 0, "bf16"),     # every expert routed by every token
     (40, 64, 2, 256, 128, 8, 9, 0, "bf16"),     # mostly empty experts
+    (50, 8, 2, 384, 256, 2, 8, 0, "bf16"),      # 8-bit: 6 groups (gate, up), 4 (down)
 ])
 def test_moe_prefill_small(T, E, k, H, I, d, bits, dead, dt):
     seed = 80 + T

@@ -333,14 +333,36 @@ static hipError_t launch_rowscale(const void *x, int f32, int rows, int cols, f1
 
 static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-// Tile height (32-row blocks): the smallest compiled height that holds the
+// How well the launches of a tile height fit in LDS: the lower of the grouped
+// GEMMs' levels (gemm_fit: 0 = no, 1 = yes, 2 = with loads in flight across
+// K steps).  For the FFN: gate and up together (or, failing that, apart) and
+// the down projection.
+static int mb_level(const TensorDev &t, bool ffn, const TensorDev *dn, int mb)
+{
+    int lv = gemm_fit(t.d, t.bits, ffn ? 2 : 1, mb, t.rows);
+    if (ffn && lv == 0)
+        lv = gemm_fit(t.d, t.bits, 1, mb, t.rows);
+    if (dn)
+        lv = std::min(lv, gemm_fit(dn->d, dn->bits, 1, mb, dn->rows));
+    return lv;
+}
+
+// Tile height (32-row blocks): the smallest of 2 .. 5 that holds the
 // expected largest expert block (mean + 2 standard deviations of a binomial
-// count) in one tile.
-static int pick_mb(int64_t rows, int E)
+// count) in one tile, lowered while a smaller height keeps loads in flight
+// across K steps and this one does not; larger blocks take several tiles.
+static int pick_mb(int64_t rows, int E, const TensorDev &t, bool ffn, const TensorDev *dn)
 {
     const double mean = (double)rows / E;
     const double big = mean + 2.0 * sqrt(mean);
-    return big <= 64.0 ? 2 : (big <= 128.0 ? 4 : 5);
+    const int want = big <= 64.0 ? 2 : (big <= 96.0 ? 3 : (big <= 128.0 ? 4 : 5));
+    for (int mb = want; mb >= 2; --mb)
+        if (mb_level(t, ffn, dn, mb) == 2)
+            return mb;
+    for (int mb = want; mb >= 2; --mb)
+        if (mb_level(t, ffn, dn, mb) >= 1)
+            return mb;
+    return 2;
 }
 
 static int64_t max_tiles(int64_t rows, int E, int mt)
@@ -351,7 +373,7 @@ static int64_t max_tiles(int64_t rows, int E, int mt)
 // gate and up in one launch unless their codebooks leave no room for the ring
 static bool fused_gate_up(const TensorDev &g, int mb)
 {
-    return gemm_fits(g.d, g.bits, 2, mb);
+    return gemm_fits(g.d, g.bits, 2, mb, g.rows);
 }
 
 static hipError_t launch_gemm(const TensorDev &t0, const TensorDev *t1, int mb, const f16 *act,
@@ -406,7 +428,7 @@ struct GemmWs {
 static GemmWs gemm_ws(const TensorDev &t, int n_x_rows)
 {
     GemmWs w;
-    w.mb = pick_mb(n_x_rows, t.n_experts);
+    w.mb = pick_mb(n_x_rows, t.n_experts, t, false, nullptr);
     w.cap = max_tiles(n_x_rows, t.n_experts, 32 * w.mb);
     size_t o = 0;
     w.tiles = o;
@@ -433,7 +455,7 @@ hipError_t launch_expert_gemm(const TensorDev &t, int n_x_rows, const void *x, i
     if (t.n_experts > kMaxRouteExperts)
         return hipErrorNotSupported;
     const GemmWs w = gemm_ws(t, n_x_rows);
-    if (!gemm_fits(t.d, t.bits, 1, w.mb))
+    if (!gemm_fits(t.d, t.bits, 1, w.mb, t.rows))
         return hipErrorNotSupported;
     char *base = static_cast<char *>(ws);
     int32_t *tiles = reinterpret_cast<int32_t *>(base + w.tiles);
@@ -475,7 +497,7 @@ static FfnWs ffn_ws(const TensorDev &g, const TensorDev &dn, int n_tok, int top_
 {
     FfnWs w;
     const int64_t P = (int64_t)n_tok * top_k;
-    w.mb = pick_mb(P, g.n_experts);
+    w.mb = pick_mb(P, g.n_experts, g, true, &dn);
     w.cap = max_tiles(P, g.n_experts, 32 * w.mb);
     w.fused = fused_gate_up(g, w.mb);
     size_t o = 0;
@@ -513,7 +535,7 @@ hipError_t launch_moe_prefill(const TensorDev &g, const TensorDev &u, const Tens
     if (g.n_experts > kMaxRouteExperts)
         return hipErrorNotSupported;
     const FfnWs w = ffn_ws(g, dn, n_tok, top_k);
-    if (!gemm_fits(g.d, g.bits, 1, w.mb) || !gemm_fits(dn.d, dn.bits, 1, w.mb))
+    if (!gemm_fits(g.d, g.bits, 1, w.mb, g.rows) || !gemm_fits(dn.d, dn.bits, 1, w.mb, dn.rows))
         return hipErrorNotSupported;
     char *base = static_cast<char *>(ws);
     int32_t *offs = reinterpret_cast<int32_t *>(base + w.offs);

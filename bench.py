@@ -238,18 +238,20 @@ def main():
     if args.workload in synth.FIT_WORKLOADS:
         return bench_fit(args, synth.FIT_WORKLOADS[args.workload])
     wl = synth.WORKLOADS[args.workload]
-    prefill = wl.n_tok > 16
-    family = "prefill" if prefill else "decode"
-    K = args.steps if args.steps is not None else (20 if prefill else 200)
-    W = args.warmup if args.warmup is not None else (3 if prefill else 20)
-    n_k = args.kernel_launches if args.kernel_launches is not None else (10 if prefill else 100)
-    n_steps = K + W
 
     # ---- layer, copies, per-step inputs (all resident before timing) ---------------
     # n_steps inputs for the timed steps, then n_k more for the dominant
     # kernel's timing loop (every launch there has its own routes too)
     t0 = time.perf_counter()
     gate_h, up_h, down_h = synth.make_moe_layer(wl)
+    base = [vq.VQTensor.from_host(t) for t in (gate_h, up_h, down_h)]
+    # the engine the library runs for this batch decides the metric
+    prefill = vq.vq_moe_ffn_engine(*base, wl.n_tok, wl.top_k) == vq.VQ_ENGINE_MFMA
+    family = "prefill" if prefill else "decode"
+    K = args.steps if args.steps is not None else (20 if prefill else 200)
+    W = args.warmup if args.warmup is not None else (3 if prefill else 20)
+    n_k = args.kernel_launches if args.kernel_launches is not None else (10 if prefill else 100)
+    n_steps = K + W
     layer_bytes = sum(t.stored_bytes() for t in (gate_h, up_h, down_h))
     xs, ids, ws = [], [], []
     for i in range(n_steps + n_k):
@@ -294,7 +296,6 @@ def main():
     if not args.layers and L * layer_bytes > MAX_COPY_BYTES:
         L = max(2, MAX_COPY_BYTES // layer_bytes)
         log(f"[bench] WARNING: layer copies capped at {L} ({L * layer_bytes / 1e9:.1f} GB)")
-    base = [vq.VQTensor.from_host(t) for t in (gate_h, up_h, down_h)]
     layers = [base] + [[t.clone() for t in base] for _ in range(L - 1)]
     x_dev = torch.from_numpy(np.stack(xs).view(np.int16)).view(torch.bfloat16).cuda()
     ids_dev = torch.from_numpy(np.stack(ids)).cuda()
@@ -484,7 +485,7 @@ def main():
             "workload": args.workload, "experts": wl.n_experts, "top_k": wl.top_k,
             "hidden": wl.hidden, "inter": wl.inter, "d": wl.d, "bits": wl.bits,
             "K": 1 << wl.bits, "tokens": wl.n_tok, "dead_row_fraction": wl.dead_frac,
-            "layer_copies": L, "hip_graph": use_graph, "graph_replay_bit_equal": graph_check,
+            "engine": "mfma" if prefill else "decode", "layer_copies": L, "hip_graph": use_graph, "graph_replay_bit_equal": graph_check,
             "peak_frac": round(frac, 4),
             ("flops_per_step" if prefill else "bytes_per_step"): int(total / K),
         },

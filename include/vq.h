@@ -127,7 +127,12 @@ vq_status vq_row_gather(const vq_tensor *W, int64_t n, const int64_t *ids, float
 
 /* ---- decode: one expert, a few tokens ---------------------------------- */
 
-/* y[n][r] = sum_c W_e[r][c] * x[n][c] for n < n_tokens (0..64), fp32 out.
+/* Card "Qwen3.8-Flash-Next-VQ-4.4bpw", changelog entry "2026-09 — bundle
+   refresh": the runtime's decode-time expert kernels read an expert's packed
+   codes straight from memory, with the activations read directly and a
+   SIMD-wide sum; card "GLM-5.3-Flash-VQ-2.7bpw", Limitations: small-batch
+   decode is where the format's kernels are least settled.
+     y[n][r] = sum_c W_e[r][c] * x[n][c] for n < n_tokens (0..64), fp32 out.
    x: [n_tokens][cols] in x_dtype; y: [n_tokens][rows] fp32.  Dead rows
    write +0.0.  Bandwidth-bound path (HBM roofline). */
 vq_status vq_expert_gemv(const vq_tensor *W, int32_t expert, int32_t n_tokens,
@@ -135,7 +140,12 @@ vq_status vq_expert_gemv(const vq_tensor *W, int32_t expert, int32_t n_tokens,
 
 /* ---- prefill: grouped GEMM over experts ---------------------------------- */
 
-/* Rows of x are grouped by expert: rows [expert_offsets[e], expert_offsets[e+1])
+/* Card "gemma-4-26b-a4b-it-VQ-6.2bpw", section "Faster prefill (optional)":
+   for long prompts the runtime turns the experts' codes into weights a chunk
+   at a time before its matmul; card "Qwen3.8-Flash-Next-VQ-4.4bpw",
+   changelog 2026-09-09: prefill kernel arms are chosen per geometry (large
+   codebooks, d = 8).  Here one launch serves every expert of a batch.
+   Rows of x are grouped by expert: rows [expert_offsets[e], expert_offsets[e+1])
    use expert e.  y[i][r] = sum_c W_e[r][c] * x[i][c], fp32, dead rows +0.0.
    expert_offsets: device int32 [n_experts+1], non-decreasing, from 0 to
    n_x_rows.  x: [n_x_rows][cols]; y: [n_x_rows][rows].  MFMA path with
@@ -148,22 +158,41 @@ vq_status vq_expert_gemm(const vq_tensor *W, int32_t n_x_rows, const void *x, vq
 
 /* ---- the routed SwiGLU expert FFN ----------------------------------------- */
 
-/* For each token t and slot s < top_k with expert e = topk_ids[t][s]:
+/* The models on the cards are mixture-of-experts transformers whose routed
+   experts are the VQ tensors (card "gemma-4-26b-a4b-it-VQ-6.2bpw", section
+   "How it was built": the experts hold most of the language model's bytes
+   and are the vector-quantized part; card "Qwen3.8-Flash-Next-VQ-4.4bpw",
+   changelog 2026-09 memory notes: a token touches only its routed experts).
+   The pages do not spell out the expert MLP or how routed outputs combine;
+   this call takes the plainest reading, a gated (SwiGLU) MLP per expert and
+   a weighted sum over the token's top_k routed experts:
+   For each token t and slot s < top_k with expert e = topk_ids[t][s]:
      g = W_gate_e x_t,  u = W_up_e x_t,  h = silu(g) * u  (silu(z) = z/(1+e^-z)),
      y[t] = sum_s topk_weights[t][s] * (W_down_e h).
    Shapes: gate, up: rows = inter, cols = hidden; down: rows = hidden,
    cols = inter; all three share n_experts.  x: [n_tokens][hidden] in
    x_dtype; topk_ids int32 and topk_weights fp32 [n_tokens][top_k];
-   y: [n_tokens][hidden] fp32.  n_tokens <= 16 takes the bandwidth-bound
-   decode kernels (the three stages below, in order), larger batches the
-   grouped MFMA GEMM.  workspace: device,
-   at least vq_moe_ffn_workspace_size() bytes, 256-byte aligned. */
+   y: [n_tokens][hidden] fp32.  The bandwidth-bound decode kernels (the
+   three stages below, in order) run every batch of up to 16 tokens, and
+   larger batches of at most 176 routed pairs (n_tokens*top_k) with hidden
+   and inter at most 8192; other batches run the grouped MFMA GEMM
+   (vq_moe_ffn_engine says which).  workspace: device, at least vq_moe_ffn_workspace_size() bytes,
+   256-byte aligned. */
 size_t vq_moe_ffn_workspace_size(const vq_tensor *gate, const vq_tensor *up,
                                  const vq_tensor *down, int32_t n_tokens, int32_t top_k);
 vq_status vq_moe_ffn(const vq_tensor *gate, const vq_tensor *up, const vq_tensor *down,
                      int32_t n_tokens, int32_t top_k, const void *x, vq_dtype x_dtype,
                      const int32_t *topk_ids, const float *topk_weights, float *y,
                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* The engine vq_moe_ffn runs for these arguments: *engine = VQ_ENGINE_DECODE
+   (the three small-batch stages) or VQ_ENGINE_MFMA (the grouped GEMM).  Host
+   only: no device work, no device pointers.  Errors as vq_moe_ffn's
+   argument checks. */
+#define VQ_ENGINE_DECODE 0
+#define VQ_ENGINE_MFMA 1
+vq_status vq_moe_ffn_engine(const vq_tensor *gate, const vq_tensor *up, const vq_tensor *down,
+                            int32_t n_tokens, int32_t top_k, int32_t *engine);
 
 /* vq_moe_ffn for callers that cannot allocate device memory (code under HIP
    graph capture, tight serving loops, harnesses that forbid hipMalloc): the
@@ -172,9 +201,9 @@ vq_status vq_moe_ffn(const vq_tensor *gate, const vq_tensor *up, const vq_tensor
    (64 MiB) that every GPU the library runs on holds from the library's load
    until the process ends.  Nothing is allocated or freed in the call.  A
    call whose vq_moe_ffn_workspace_size() exceeds the array returns
-   VQ_ERR_UNSUPPORTED (that covers every decode batch up to 16 tokens x
-   1024 routed pairs of hidden + inter <= 16384, and prefill batches of a few
-   hundred routed pairs).  All calls on one GPU share its array: calls that
+   VQ_ERR_UNSUPPORTED (that covers every batch on the decode kernels up to
+   1024 routed pairs of hidden + inter <= 16384, and batches on the grouped
+   GEMM of a few hundred routed pairs).  All calls on one GPU share its array: calls that
    overlap on that GPU (several streams or threads at once) race and give
    undefined output; calls in order on one stream are safe.  The array's
    address is looked up on the first call on each device (with that device

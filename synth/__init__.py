@@ -229,6 +229,16 @@ WORKLOADS = {
         "moe_decode_e512_h4096_i1024_d2k1024_b1", 512, 10, 4096, 1024, 2, 10, 1, seed=1237),
     "moe_decode_e512_h4096_i1024_d2k1024_b8": MoEWorkload(
         "moe_decode_e512_h4096_i1024_d2k1024_b8", 512, 10, 4096, 1024, 2, 10, 8, seed=1237),
+    # Batches between decode and prefill (multi-token verify steps, short
+    # prompts): the decode geometries at 17, 32 and 64 tokens, and the 128-
+    # expert one up to 128 tokens (4 routed pairs per expert at 64 tokens);
+    # 16 tokens is the last batch the decode kernels take by count alone.
+    **{f"moe_batch_e512_h4096_i1024_d2k256_t{t}": MoEWorkload(
+        f"moe_batch_e512_h4096_i1024_d2k256_t{t}", 512, 10, 4096, 1024, 2, 8, t, seed=1240 + t)
+       for t in (16, 17, 32, 64)},
+    **{f"moe_batch_e128_h2048_i768_d4k512_t{t}": MoEWorkload(
+        f"moe_batch_e128_h2048_i768_d4k512_t{t}", 128, 8, 2048, 768, 4, 9, t, seed=1240 + t)
+       for t in (17, 32, 64, 128)},
     # Prefill: 2048 tokens, 128 experts top-8, d=4/K=2048 11-bit.
     "moe_prefill_e128_h2816_i704_d4k2048_t2048": MoEWorkload(
         "moe_prefill_e128_h2816_i704_d4k2048_t2048", 128, 8, 2816, 704, 4, 11, 2048, seed=1238),

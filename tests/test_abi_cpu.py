@@ -202,3 +202,33 @@ def test_noalloc_refuses_batches_beyond_its_array(lib):
     # argument errors come first, as in vq_moe_ffn
     st = lib.vq_moe_ffn_noalloc(*args, 2048, 65, FAKE, 1, FAKE, FAKE, FAKE, None)
     assert st == 1 and "top_k" in lib.vq_last_error().decode()
+
+
+def test_ffn_engine_choice(lib):
+    """vq_moe_ffn_engine (host only): the decode kernels for up to 16 tokens,
+    and past that for at most 176 routed pairs with hidden and inter at most
+    8192; the grouped GEMM otherwise."""
+    def engine(T, k, E, H=4096, I=1024):
+        g = _t(rows=I, cols=H, n_experts=E, n_stored=E * I)
+        u = _t(rows=I, cols=H, n_experts=E, n_stored=E * I)
+        dn = _t(rows=H, cols=I, n_experts=E, n_stored=E * H)
+        out = ctypes.c_int32(-1)
+        st = lib.vq_moe_ffn_engine(ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), T, k,
+                                   ctypes.byref(out))
+        assert st == 0, lib.vq_last_error().decode()
+        return out.value
+    D, M = vq.VQ_ENGINE_DECODE, vq.VQ_ENGINE_MFMA
+    assert engine(0, 8, 128) == D and engine(1, 10, 512) == D and engine(16, 10, 512) == D
+    assert engine(16, 64, 64, H=1024, I=512) == D    # 1024 pairs: by token count
+    assert engine(17, 10, 512) == D       # 170 pairs
+    assert engine(18, 10, 512) == M       # 180 pairs
+    assert engine(22, 8, 128) == D        # 176 pairs
+    assert engine(23, 8, 128) == M
+    assert engine(17, 8, 128, H=16384) == M   # hidden past the decode kernels
+    assert engine(2048, 8, 128) == M
+    # bad arguments: vq_moe_ffn's checks
+    g = _t(rows=1024, cols=4096, n_experts=8, n_stored=8 * 1024)
+    out = ctypes.c_int32(-1)
+    st = lib.vq_moe_ffn_engine(ctypes.byref(g), ctypes.byref(g), ctypes.byref(g), 4, 2,
+                               ctypes.byref(out))
+    assert st == 1 and "down" in lib.vq_last_error().decode()

@@ -185,6 +185,47 @@ def test_moe_decode_maximum_sizes(T, E, k, H, I):
     check_close(y, oracle.moe_ffn(gate, up, down, x, ids, w), f"max T={T} k={k} H={H}")
 
 
+# --------------------------------------------------------------------------
+# batches past 16 tokens: the decode kernels up to 176 routed pairs
+# --------------------------------------------------------------------------
+
+def _engine(gate, up, down, T, k):
+    return vq.vq_moe_ffn_engine(_dev(gate), _dev(up), _dev(down), T, k)
+
+
+@pytest.mark.parametrize("name,engine", [
+    ("moe_batch_e512_h4096_i1024_d2k256_t17", vq.VQ_ENGINE_DECODE),   # 170 pairs
+    ("moe_batch_e512_h4096_i1024_d2k256_t32", vq.VQ_ENGINE_MFMA),
+    ("moe_batch_e512_h4096_i1024_d2k256_t64", vq.VQ_ENGINE_MFMA),
+])
+def test_moe_batch_full_size(name, engine):
+    """17, 32 and 64 tokens on the 512-expert top-10 layer (0.3 to 1.25
+    routed pairs per expert); every token is checked."""
+    wl = synth.WORKLOADS[name]
+    gate, up, down, x, ids, w = _moe_case(wl)
+    assert _engine(gate, up, down, wl.n_tok, wl.top_k) == engine
+    y = _run_moe(gate, up, down, x, ids, w)
+    check_close(y, oracle.moe_ffn(gate, up, down, x, ids, w), name)
+
+
+@pytest.mark.parametrize("T,engine", [
+    (44, vq.VQ_ENGINE_DECODE),    # 176 routed pairs
+    (45, vq.VQ_ENGINE_MFMA),      # 180
+])
+def test_moe_batch_engine_boundary(T, engine):
+    """Either side of the engine switch: same layer, both engines, both
+    against the oracle."""
+    E, k, H, I = 32, 4, 256, 128
+    wl = synth.MoEWorkload("boundary", E, k, H, I, 4, 9, T, seed=95)
+    gate = synth.make_tensor(wl.seed, 1, rows=I, cols=H, d=4, bits=9, n_experts=E, dead_rows=2)
+    up = synth.make_tensor(wl.seed, 2, rows=I, cols=H, d=4, bits=9, n_experts=E)
+    down = synth.make_tensor(wl.seed, 3, rows=H, cols=I, d=4, bits=9, n_experts=E, dead_rows=4)
+    x, ids, w = synth.make_moe_inputs(wl, 0)
+    assert _engine(gate, up, down, T, k) == engine
+    y = _run_moe(gate, up, down, x, ids, w)
+    check_close(y, oracle.moe_ffn(gate, up, down, x, ids, w), f"T={T}")
+
+
 def test_moe_decode_repeated_expert_in_token():
     """An id repeated within a token is served as two slots of one expert."""
     E, k, H, I = 4, 3, 128, 64

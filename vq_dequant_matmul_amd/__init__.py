@@ -82,6 +82,7 @@ def load_library():
         "vq_expert_gemm_workspace_size": (SZ, [T, I32]),
         "vq_expert_gemm": (ctypes.c_int, [T, I32, P, ctypes.c_int, P, P, P, SZ, P]),
         "vq_moe_ffn_workspace_size": (SZ, [T, T, T, I32, I32]),
+        "vq_moe_ffn_engine": (ctypes.c_int, [T, T, T, I32, I32, P]),
         "vq_moe_ffn": (ctypes.c_int, [T, T, T, I32, I32, P, ctypes.c_int, P, P, P, P, SZ, P]),
         "vq_moe_ffn_noalloc": (ctypes.c_int, [T, T, T, I32, I32, P, ctypes.c_int, P, P, P, P]),
         "vq_moe_gate_up": (ctypes.c_int, [T, T, I32, I32, P, ctypes.c_int, P, P, P]),
@@ -302,6 +303,21 @@ def vq_moe_ffn_workspace_size(gate: VQTensor, up: VQTensor, down: VQTensor, n_to
                                                         ctypes.byref(d), n_tokens, top_k))
 
 
+VQ_ENGINE_DECODE = 0
+VQ_ENGINE_MFMA = 1
+
+
+def vq_moe_ffn_engine(gate: VQTensor, up: VQTensor, down: VQTensor, n_tokens: int,
+                      top_k: int) -> int:
+    """VQ_ENGINE_DECODE or VQ_ENGINE_MFMA: the engine vq_moe_ffn runs for
+    this batch (host only)."""
+    g, u, d = gate.c(), up.c(), down.c()
+    eng = ctypes.c_int32(-1)
+    _check(load_library().vq_moe_ffn_engine(ctypes.byref(g), ctypes.byref(u), ctypes.byref(d),
+                                            n_tokens, top_k, ctypes.byref(eng)))
+    return int(eng.value)
+
+
 def vq_moe_ffn(gate: VQTensor, up: VQTensor, down: VQTensor, x: torch.Tensor,
                topk_ids: torch.Tensor, topk_weights: torch.Tensor,
                out: Optional[torch.Tensor] = None,
@@ -435,7 +451,8 @@ __all__ = [
     "VQError", "VQTensor", "build", "load_library", "vq_validate", "vq_dequantize",
     "vq_row_gather", "vq_fit",
     "vq_expert_gemv", "vq_expert_gemm", "vq_expert_gemm_workspace_size", "vq_moe_ffn",
-    "vq_moe_ffn_workspace_size", "vq_moe_ffn_noalloc", "vq_moe_gate_up", "vq_moe_down", "vq_moe_combine",
+    "vq_moe_ffn_workspace_size", "vq_moe_ffn_noalloc", "vq_moe_ffn_engine",
+    "VQ_ENGINE_DECODE", "VQ_ENGINE_MFMA", "vq_moe_gate_up", "vq_moe_down", "vq_moe_combine",
     "vq_set_kernel_events", "vq_moe_stack", "vq_moe_stack_workspace_size",
     "VQ_F32", "VQ_BF16",
 ]

@@ -126,6 +126,19 @@ DecodeWs decode_ws(const vq_tensor &g, const vq_tensor &dn, int n_tok, int top_k
 constexpr int kDecodeMaxTokens = 16;
 constexpr int kGemvMaxTokens = 64;
 
+// Past kDecodeMaxTokens tokens the routed FFN stays on the decode kernels
+// while the batch has at most this many routed pairs.  The decode kernels
+// cost about the same per pair at any batch size (every pair streams its
+// expert's rows), while the grouped GEMM reads an expert once per tile of
+// its pairs but pays a fixed cost per call (routing, row scaling, the
+// combine, tiles of 64 rows that small batches leave mostly empty).  On the
+// 512-expert top-10 layer (6.3 MB per routed expert) the two cost the same
+// near 190 pairs, on the 128-expert top-8 one (1.3 MB) near 165.
+#ifndef VQ_DECODE_MAX_PAIRS
+#define VQ_DECODE_MAX_PAIRS 176
+#endif
+constexpr int kDecodeMaxPairs = VQ_DECODE_MAX_PAIRS;
+
 }  // namespace
 
 namespace vq {
@@ -495,6 +508,20 @@ static vq_status check_ffn(const vq_tensor *gate, const vq_tensor *up, const vq_
     return VQ_OK;
 }
 
+// Which engine runs the routed FFN (arguments already checked): the decode
+// kernels for up to kDecodeMaxTokens tokens (whose size limits then apply),
+// and for larger batches of at most kDecodeMaxPairs routed pairs whose
+// columns fit the decode kernels; otherwise the grouped MFMA GEMM.
+static bool ffn_uses_decode(const vq_tensor &gate, const vq_tensor &down, int32_t n_tokens,
+                            int32_t top_k)
+{
+    if (n_tokens <= kDecodeMaxTokens)
+        return true;
+    const int64_t pairs = (int64_t)n_tokens * top_k;
+    return pairs <= kDecodeMaxPairs && pairs <= vq::kMaxSlots &&
+           gate.cols / 64 <= vq::kMaxGroupsDecode && down.cols / 64 <= vq::kMaxGroupsDecode;
+}
+
 // Size limits of the grouped-GEMM path: routed pairs are counted in int32,
 // and every activation matrix the GEMM reads (x rows, then one h row per
 // routed pair) is indexed in 32-bit bytes.
@@ -543,12 +570,25 @@ VQ_EXPORT size_t vq_moe_ffn_workspace_size(const vq_tensor *gate, const vq_tenso
 {
     if (check_ffn(gate, up, down, n_tokens, top_k) != VQ_OK)
         return 0;
-    if (n_tokens <= kDecodeMaxTokens)
+    if (ffn_uses_decode(*gate, *down, n_tokens, top_k))
         return decode_ws(*gate, *down, n_tokens, top_k).total;
     if (check_prefill_sizes(*gate, n_tokens, top_k) != VQ_OK)
         return 0;
     return vq::moe_prefill_workspace_bytes(vq::to_dev(*gate), vq::to_dev(*up), vq::to_dev(*down),
                                            n_tokens, top_k);
+}
+
+VQ_EXPORT vq_status vq_moe_ffn_engine(const vq_tensor *gate, const vq_tensor *up,
+                                      const vq_tensor *down, int32_t n_tokens, int32_t top_k,
+                                      int32_t *engine)
+{
+    vq_status st = check_ffn(gate, up, down, n_tokens, top_k);
+    if (st != VQ_OK)
+        return st;
+    if (!engine)
+        return fail(VQ_ERR_INVALID_ARGUMENT, "engine must be non-NULL");
+    *engine = ffn_uses_decode(*gate, *down, n_tokens, top_k) ? VQ_ENGINE_DECODE : VQ_ENGINE_MFMA;
+    return ok();
 }
 
 VQ_EXPORT vq_status vq_moe_ffn(const vq_tensor *gate, const vq_tensor *up, const vq_tensor *down,
@@ -572,7 +612,7 @@ VQ_EXPORT vq_status vq_moe_ffn(const vq_tensor *gate, const vq_tensor *up, const
     hipStream_t s = static_cast<hipStream_t>(stream);
     const vq::TensorDev g = vq::to_dev(*gate), u = vq::to_dev(*up), dn = vq::to_dev(*down);
 
-    if (n_tokens > kDecodeMaxTokens) {
+    if (!ffn_uses_decode(*gate, *down, n_tokens, top_k)) {
         if ((st = check_prefill_sizes(*gate, n_tokens, top_k)) != VQ_OK)
             return st;
         const size_t need = vq::moe_prefill_workspace_bytes(g, u, dn, n_tokens, top_k);
@@ -648,7 +688,8 @@ VQ_EXPORT vq_status vq_moe_ffn_noalloc(const vq_tensor *gate, const vq_tensor *u
         return st;
     if (n_tokens == 0)
         return ok();
-    if (n_tokens > kDecodeMaxTokens && (st = check_prefill_sizes(*gate, n_tokens, top_k)) != VQ_OK)
+    if (!ffn_uses_decode(*gate, *down, n_tokens, top_k) &&
+        (st = check_prefill_sizes(*gate, n_tokens, top_k)) != VQ_OK)
         return st;
     const size_t need = vq_moe_ffn_workspace_size(gate, up, down, n_tokens, top_k);
     if (need > (size_t)VQ_NOALLOC_SCRATCH_BYTES)

@@ -311,6 +311,23 @@ vq_status vq_fit(int64_t n_rows, int32_t cols, int32_t d, int32_t bits, int32_t 
    the caller. */
 vq_status vq_set_kernel_events(void *start, void *stop);
 
+/* ---- ceiling probes (measurement only) ---------------------------------- */
+
+/* Streaming read of buf (device, 16-byte aligned, bytes a multiple of 16)
+   by n_workgroups workgroups of 256 lanes, each lane loading 16 bytes per
+   load with four loads in flight; out: device uint32 [n_workgroups*256]
+   receives an xor of what each lane read.  Times the best-case HBM read
+   rate of the device, the ceiling beside the 8 TB/s published peak. */
+vq_status vq_probe_read(const void *buf, size_t bytes, int32_t n_workgroups, uint32_t *out,
+                        void *stream);
+
+/* iters x 4 dependent-chain-free v_mfma_f32_32x32x16_f16 per wave on
+   register operands (32768 flops each), n_workgroups workgroups of four
+   waves, no memory traffic; out: device fp32 [n_workgroups*256].  Times the
+   fp16 matrix-core rate the device holds, the ceiling beside the
+   2.5 PFLOP/s published dense peak. */
+vq_status vq_probe_mfma(int32_t n_workgroups, int32_t iters, float *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

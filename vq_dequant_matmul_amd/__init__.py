@@ -83,6 +83,8 @@ def load_library():
         "vq_expert_gemm": (ctypes.c_int, [T, I32, P, ctypes.c_int, P, P, P, SZ, P]),
         "vq_moe_ffn_workspace_size": (SZ, [T, T, T, I32, I32]),
         "vq_moe_ffn_engine": (ctypes.c_int, [T, T, T, I32, I32, P]),
+        "vq_probe_read": (ctypes.c_int, [P, SZ, I32, P, P]),
+        "vq_probe_mfma": (ctypes.c_int, [I32, I32, P, P]),
         "vq_moe_ffn": (ctypes.c_int, [T, T, T, I32, I32, P, ctypes.c_int, P, P, P, P, SZ, P]),
         "vq_moe_ffn_noalloc": (ctypes.c_int, [T, T, T, I32, I32, P, ctypes.c_int, P, P, P, P]),
         "vq_moe_gate_up": (ctypes.c_int, [T, T, I32, I32, P, ctypes.c_int, P, P, P]),
@@ -318,6 +320,19 @@ def vq_moe_ffn_engine(gate: VQTensor, up: VQTensor, down: VQTensor, n_tokens: in
     return int(eng.value)
 
 
+def vq_probe_read(buf: torch.Tensor, n_workgroups: int, out: torch.Tensor) -> None:
+    """Streaming-read ceiling probe over buf (device, any dtype); out: device
+    uint32/int32 of n_workgroups*256 entries."""
+    _check(load_library().vq_probe_read(_ptr(buf), buf.numel() * buf.element_size(),
+                                        n_workgroups, _ptr(out), _stream()))
+
+
+def vq_probe_mfma(n_workgroups: int, iters: int, out: torch.Tensor) -> None:
+    """MFMA-only ceiling probe: iters x 4 v_mfma_f32_32x32x16_f16 per wave;
+    out: device fp32 of n_workgroups*256 entries."""
+    _check(load_library().vq_probe_mfma(n_workgroups, iters, _ptr(out), _stream()))
+
+
 def vq_moe_ffn(gate: VQTensor, up: VQTensor, down: VQTensor, x: torch.Tensor,
                topk_ids: torch.Tensor, topk_weights: torch.Tensor,
                out: Optional[torch.Tensor] = None,
@@ -453,6 +468,7 @@ __all__ = [
     "vq_expert_gemv", "vq_expert_gemm", "vq_expert_gemm_workspace_size", "vq_moe_ffn",
     "vq_moe_ffn_workspace_size", "vq_moe_ffn_noalloc", "vq_moe_ffn_engine",
     "VQ_ENGINE_DECODE", "VQ_ENGINE_MFMA", "vq_moe_gate_up", "vq_moe_down", "vq_moe_combine",
+    "vq_probe_read", "vq_probe_mfma",
     "vq_set_kernel_events", "vq_moe_stack", "vq_moe_stack_workspace_size",
     "VQ_F32", "VQ_BF16",
 ]

@@ -191,6 +191,32 @@ VQ_EXPORT const char *vq_status_string(vq_status s)
 
 VQ_EXPORT const char *vq_last_error(void) { return g_last_error.c_str(); }
 
+VQ_EXPORT vq_status vq_probe_read(const void *buf, size_t bytes, int32_t n_workgroups,
+                                  uint32_t *out, void *stream)
+{
+    if (!buf || !aligned(buf, 16) || bytes % 16 != 0 || bytes == 0)
+        return fail(VQ_ERR_INVALID_ARGUMENT,
+                    "buf: must be a non-NULL, 16-byte aligned device buffer of a multiple of 16 "
+                    "bytes (got %zu bytes at %p)", bytes, buf);
+    if (n_workgroups < 1 || n_workgroups > 65536 || !out)
+        return fail(VQ_ERR_INVALID_ARGUMENT,
+                    "n_workgroups = %d: must be in [1, 65536], with out non-NULL", n_workgroups);
+    const hipError_t e = vq::launch_probe_read(buf, bytes, out, n_workgroups,
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "vq_probe_read");
+}
+
+VQ_EXPORT vq_status vq_probe_mfma(int32_t n_workgroups, int32_t iters, float *out, void *stream)
+{
+    if (n_workgroups < 1 || n_workgroups > 65536 || iters < 1 || !out)
+        return fail(VQ_ERR_INVALID_ARGUMENT,
+                    "n_workgroups = %d, iters = %d: need n_workgroups in [1, 65536], iters >= 1 "
+                    "and out non-NULL", n_workgroups, iters);
+    const hipError_t e = vq::launch_probe_mfma(n_workgroups, iters, out,
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? ok() : hip_fail(e, "vq_probe_mfma");
+}
+
 VQ_EXPORT vq_status vq_set_kernel_events(void *start, void *stop)
 {
     if ((start == nullptr) != (stop == nullptr))

@@ -51,6 +51,11 @@ hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream);
 
 // y[t][c] = sum_s w[t][s] * z[t*k + s][c], slot order (accumulate: y[t][c] +=
 // that sum).
+// ceiling probes (vq_probe.hip)
+hipError_t launch_probe_read(const void *p, size_t bytes, uint32_t *out, int n_wg,
+                             hipStream_t stream);
+hipError_t launch_probe_mfma(int n_wg, int iters, float *out, hipStream_t stream);
+
 hipError_t launch_combine(const float *z, const float *w, int n_tok, int top_k, int hidden,
                           float *y, bool accumulate, hipStream_t stream);
 

@@ -226,7 +226,9 @@ vq_status vq_moe_gate_up(const vq_tensor *gate, const vq_tensor *up, int32_t n_t
                          const int32_t *topk_ids, float *h, void *stream);
 
 /* Stage 2 (down): z[q][c] = sum_r W_down_e[c][r] * h[q][r] for every pair q;
-   dead rows of down give +0.0.  h: device fp32 [n_tokens*top_k][inter];
+   dead rows of down give +0.0.  h enters the products rounded once to
+   fp16, scaled by a power of two per (pair, 64-column group), as the
+   grouped GEMM's h does.  h: device fp32 [n_tokens*top_k][inter];
    z: device fp32 [n_tokens*top_k][hidden]. */
 vq_status vq_moe_down(const vq_tensor *down, int32_t n_tokens, int32_t top_k, const float *h,
                       const int32_t *topk_ids, float *z, void *stream);

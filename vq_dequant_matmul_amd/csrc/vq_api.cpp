@@ -496,7 +496,7 @@ static hipError_t launch_down(const vq::TensorDev &dn, int n_tokens, int top_k, 
     L.t[0] = dn;
     L.nproj = 1;
     L.act = h;
-    L.act_f32 = 1;
+    L.act_f32 = 2;   // h rounded once to fp16, as in the fused down+combine kernel
     L.act_stride = dn.cols;
     L.out = z;
     L.out_stride = dn.rows;

@@ -208,10 +208,20 @@ __device__ __forceinline__ float segment_sum_dpp(float v, int S)
         v += dpp_move<0x141>(v);   // row_half_mirror
     if (S >= 16)
         v += dpp_move<0x140>(v);   // row_mirror
-    if (S >= 32)
-        v += __shfl_xor(v, 16, 64);
-    if (S >= 64)
-        v += __shfl_xor(v, 32, 64);
+    // across 16-lane rows: v_permlane16_swap / v_permlane32_swap exchange
+    // rows (halves) between two registers without going through LDS.  With
+    // both operands v, the two results hold the pair's two rows (halves) in
+    // every lane, so their sum is the same in all lanes.
+    if (S >= 32) {
+        const uint32_t u = __float_as_uint(v);
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    if (S >= 64) {
+        const uint32_t u = __float_as_uint(v);
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
     return v;
 }
 

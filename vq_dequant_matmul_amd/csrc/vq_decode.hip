@@ -32,7 +32,7 @@ namespace vq {
 // Per-subvector-length instantiations live in vq_decode_d{2,4,8}.hip so they
 // compile in parallel.
 #define VQ_DECL_D(N)                                                                         \
-    extern template hipError_t rows_d<N>(int, const RowsArgs &, int, int, bool, int64_t, int, \
+    extern template hipError_t rows_d<N>(int, const RowsArgs &, int, int, int, int64_t, int, \
                                          size_t, hipStream_t);                                \
     extern template hipError_t dequantize_d<N>(const TensorDev &, int, float *, hipStream_t); \
     extern template hipError_t mix_d<N>(int, const MixArgs &, size_t, hipStream_t);
@@ -187,9 +187,9 @@ hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream)
     const int64_t units = (int64_t)P * a.tiles;
     const int n_cu = cu_count();
     switch (t0.d) {
-    case 2: return rows_d<2>(t0.bits, a, gpl, L.nproj, L.act_f32 != 0, units, n_cu, lds, stream);
-    case 4: return rows_d<4>(t0.bits, a, gpl, L.nproj, L.act_f32 != 0, units, n_cu, lds, stream);
-    case 8: return rows_d<8>(t0.bits, a, gpl, L.nproj, L.act_f32 != 0, units, n_cu, lds, stream);
+    case 2: return rows_d<2>(t0.bits, a, gpl, L.nproj, L.act_f32, units, n_cu, lds, stream);
+    case 4: return rows_d<4>(t0.bits, a, gpl, L.nproj, L.act_f32, units, n_cu, lds, stream);
+    case 8: return rows_d<8>(t0.bits, a, gpl, L.nproj, L.act_f32, units, n_cu, lds, stream);
     default: return hipErrorInvalidValue;
     }
 }

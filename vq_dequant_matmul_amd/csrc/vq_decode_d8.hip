@@ -3,7 +3,7 @@
 
 namespace vq {
 
-template hipError_t rows_d<8>(int, const RowsArgs &, int, int, bool, int64_t, int, size_t,
+template hipError_t rows_d<8>(int, const RowsArgs &, int, int, int, int64_t, int, size_t,
                                hipStream_t);
 template hipError_t dequantize_d<8>(const TensorDev &, int, float *, hipStream_t);
 template hipError_t mix_d<8>(int, const MixArgs &, size_t, hipStream_t);

@@ -1122,18 +1122,24 @@ static hipError_t rows_launch(const RowsArgs &a, int64_t units, int n_cu, size_t
     return hipGetLastError();
 }
 
+// act: 0 bf16 activations; 1 fp32 ones, whose low bits ride along as a
+// second fp16 term; 2 fp32 ones rounded once to fp16 (one projection: the
+// down projection of h)
 template <int D, int BITS, int GPL, int NPROJ>
-static hipError_t rows_act(const RowsArgs &a, bool act_f32, int64_t units, int n_cu, size_t lds,
+static hipError_t rows_act(const RowsArgs &a, int act, int64_t units, int n_cu, size_t lds,
                            hipStream_t s)
 {
-    // fp32 activations keep their low bits as a second fp16 term
-    if (act_f32)
+    if constexpr (NPROJ == 1) {
+        if (act == 2)
+            return rows_launch<D, BITS, GPL, NPROJ, false, true>(a, units, n_cu, lds, s);
+    }
+    if (act != 0)
         return rows_launch<D, BITS, GPL, NPROJ, true, true>(a, units, n_cu, lds, s);
     return rows_launch<D, BITS, GPL, NPROJ, false, false>(a, units, n_cu, lds, s);
 }
 
 template <int D, int BITS>
-static hipError_t rows_db(const RowsArgs &a, int gpl, int nproj, bool act_f32, int64_t units,
+static hipError_t rows_db(const RowsArgs &a, int gpl, int nproj, int act_f32, int64_t units,
                           int n_cu, size_t lds, hipStream_t s)
 {
     if (gpl == 1)
@@ -1146,7 +1152,7 @@ static hipError_t rows_db(const RowsArgs &a, int gpl, int nproj, bool act_f32, i
 template <int D>
 struct RowsD {
     template <int BITS>
-    static hipError_t run(const RowsArgs &a, int gpl, int nproj, bool f32, int64_t units, int n_cu,
+    static hipError_t run(const RowsArgs &a, int gpl, int nproj, int f32, int64_t units, int n_cu,
                           size_t lds, hipStream_t s)
     {
         return rows_db<D, BITS>(a, gpl, nproj, f32, units, n_cu, lds, s);
@@ -1154,7 +1160,7 @@ struct RowsD {
 };
 
 template <int D>
-hipError_t rows_d(int bits, const RowsArgs &a, int gpl, int nproj, bool f32, int64_t units,
+hipError_t rows_d(int bits, const RowsArgs &a, int gpl, int nproj, int f32, int64_t units,
                   int n_cu, size_t lds, hipStream_t s)
 {
     VQ_BITS_SWITCH(bits, RowsD<D>::template run, a, gpl, nproj, f32, units, n_cu, lds, s)

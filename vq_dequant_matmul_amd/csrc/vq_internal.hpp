@@ -29,7 +29,8 @@ struct RowsLaunch {
     TensorDev t[2];        // one or two projections (gate, up)
     int nproj;             // 1 or 2 (2 = SwiGLU of t[0] (gate) and t[1] (up))
     const void *act;       // activations: rows of t[0].cols elements
-    int act_f32;           // 1: fp32 activations, 0: bf16 bit patterns
+    int act_f32;           // 0: bf16 bit patterns; 1: fp32 activations (hi + lo fp16
+                           // terms); 2: fp32 activations rounded once to fp16
     int64_t act_stride;    // elements between activation rows
     float *out;            // output rows
     int64_t out_stride;    // elements between output rows

@@ -162,6 +162,8 @@ static int rows_args(const RowsLaunch &L, RowsArgs &a, int &gpl)
     a.cb_offset[1] = (cb1_fixed * 4 <= 32768) ? cb1_fixed : ((L.t[0].cb_dwords + 3) & ~3);
     int off = L.nproj == 2 ? a.cb_offset[1] + L.t[1].cb_dwords : L.t[0].cb_dwords;
     off = (off + 3) & ~3;
+    if (t0.d == 2 && t0.bits == 8)   // copies of every entry (rows_banked)
+        off = kBankedCbDwords;
     a.list_offset = off;
     return off + list_dwords(P);
 }

@@ -66,6 +66,15 @@ struct RowsArgs {
 //   [list_offset, ...)   work lists (see build_lists)
 // The second codebook sits at its largest possible size when that keeps
 // the offset inside a ds_read immediate, so no lookup needs a base add.
+// 8-bit codes with d = 2: the codebooks as 16 copies per entry.  Entry k of
+// projection p owns bytes [128k + 64p, 128k + 64p + 64) of LDS and lane l
+// reads copy l % 16, so of the 32 lanes an LDS pass serves only lanes l and
+// l + 16 can meet in a bank (when their entries have equal parity), against
+// a random spread over a single copy.  32 KiB for one or two projections.
+template <int D, int BITS>
+constexpr bool rows_banked() { return D == 2 && BITS == 8; }
+constexpr int kBankedCbDwords = 8192;
+
 template <int D, int BITS>
 constexpr int cb1_fixed_dwords() { return (1 << BITS) * D / 2; }
 
@@ -305,6 +314,7 @@ __device__ __forceinline__ void compute_rows(const RowsArgs &a, const uint32_t *
         for (int p = 0; p < NPROJ; ++p) {
             part[p] = 0.0f;
             const uint32_t *cb = lds + (p == 0 ? 0 : cb1_offset<D, BITS>(a));
+            const uint32_t *cbk = lds + p * 16 + (threadIdx.x & 15);   // this lane's copies
 #pragma unroll
             for (int i = 0; i < GPL; ++i) {
                 const int g = sl + i * S;
@@ -314,7 +324,11 @@ __device__ __forceinline__ void compute_rows(const RowsArgs &a, const uint32_t *
 #pragma unroll
                 for (int t = 0; t < G; ++t) {
                     const uint32_t code = extract<BITS, NW>(nw, t);
-                    const Entry<D> en = fetch_entry<D>(cb, code);
+                    Entry<D> en;
+                    if constexpr (rows_banked<D, BITS>())
+                        en.v[0] = cbk[code * 32];
+                    else
+                        en = fetch_entry<D>(cb, code);
 #pragma unroll
                     for (int k = 0; k < HP; ++k) {
                         acc = dot2(en.v[k], xr.hi[i][t * HP + k], acc);
@@ -400,19 +414,42 @@ __device__ __forceinline__ void cb_regs_to_lds(const uint16_t *cb, int dwords, c
 template <int D, int BITS, int NPROJ>
 __device__ __forceinline__ void load_codebooks(const RowsArgs &a, CbRegs<D, BITS, NPROJ> &cr)
 {
+    if constexpr (rows_banked<D, BITS>()) {
+        // thread t holds entry t (one dword) of each projection
 #pragma unroll
-    for (int p = 0; p < NPROJ; ++p)
-        cb_to_regs(a.codebook[p], a.cb_dwords[p], cr.v[p]);
+        for (int p = 0; p < NPROJ; ++p) {
+            const int t = threadIdx.x;
+            const uint32_t v =
+                t < a.cb_dwords[p] ? reinterpret_cast<const uint32_t *>(a.codebook[p])[t] : 0u;
+            cr.v[p][0] = make_uint4(v, v, v, v);
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < NPROJ; ++p)
+            cb_to_regs(a.codebook[p], a.cb_dwords[p], cr.v[p]);
+    }
 }
 
 template <int D, int BITS, int NPROJ>
 __device__ __forceinline__ void store_codebooks(const RowsArgs &a, const CbRegs<D, BITS, NPROJ> &cr,
                                                 uint32_t *__restrict__ lds)
 {
+    if constexpr (rows_banked<D, BITS>()) {
+        static_assert(kThreads == 256, "one thread per entry");
+        // the 16 copies of entry t, 16 bytes at a time; neighbouring lanes
+        // start at different chunks so a store's lanes spread over the banks
+        char *row = reinterpret_cast<char *>(lds) + threadIdx.x * 128;
 #pragma unroll
-    for (int p = 0; p < NPROJ; ++p)
-        cb_regs_to_lds(a.codebook[p], a.cb_dwords[p], cr.v[p],
-                       lds + (p == 0 ? 0 : cb1_offset<D, BITS>(a)));
+        for (int p = 0; p < NPROJ; ++p)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *reinterpret_cast<uint4 *>(row + p * 64 + ((j + threadIdx.x) & 3) * 16) = cr.v[p][0];
+    } else {
+#pragma unroll
+        for (int p = 0; p < NPROJ; ++p)
+            cb_regs_to_lds(a.codebook[p], a.cb_dwords[p], cr.v[p],
+                           lds + (p == 0 ? 0 : cb1_offset<D, BITS>(a)));
+    }
 }
 
 // Work lists in LDS, from list_offset (P = number of pairs):
@@ -597,18 +634,34 @@ __global__ __launch_bounds__(kThreads) void k_rows(const RowsArgs a)
 
     // Units are software-pipelined two deep: the rows of unit k+1 are in
     // flight while unit k is computed (buffers A and B alternate).
-    int u = 0;
+    // The current distinct expert's list entries are kept in (scalar)
+    // registers: LDS is busy with the codebook lookups, so a unit of the same
+    // expert reads it only to pick the pair when the expert serves several.
+    int u = -1;
+    int64_t u_end = 0;   // first unit past expert u
+    int u0 = 0, nu = 1, ue = 0, uitem = 0;
     auto unit_at = [&](int64_t kk) {
-        while (kk >= (int64_t)L.ustart[u + 1] * a.tiles)
-            ++u;
-        const int u0 = L.ustart[u];
-        const int nu = L.ustart[u + 1] - u0;
+        if (kk >= u_end) {
+            do {
+                ++u;
+                u_end = (int64_t)L.ustart[u + 1] * a.tiles;
+            } while (kk >= u_end);
+            u0 = L.ustart[u];
+            nu = L.ustart[u + 1] - u0;
+            ue = L.uexp[u];
+            uitem = L.items[u0];
+        }
         const int64_t rel = kk - (int64_t)u0 * a.tiles;
-        const int t = (int)udiv_small(rel, nu);
         Unit un;
-        un.item = L.items[u0 + (int)(rel - (int64_t)t * nu)];
-        un.e = L.uexp[u];
-        un.row0 = t * a.tile_rows + wave * ITERS * rpw;
+        un.e = ue;
+        if (nu == 1) {
+            un.item = uitem;
+            un.row0 = (int)rel * a.tile_rows + wave * ITERS * rpw;
+        } else {
+            const int t = (int)udiv_small(rel, nu);
+            un.item = L.items[u0 + (int)(rel - (int64_t)t * nu)];
+            un.row0 = t * a.tile_rows + wave * ITERS * rpw;
+        }
         return un;
     };
     int cur_item = -1;

@@ -11,10 +11,14 @@
 //     and 32 weight rows per wave; a wave's weight rows are of one
 //     projection or of gate and up together (the SwiGLU product is formed in
 //     the epilogue);
-//   * the K loop walks 64-column groups through a ring of S stages in LDS,
-//     filled by direct global->LDS loads (no register staging): the tile's
-//     activation rows (fp16, already range-scaled) and every lane's own
-//     packed-code window and scale.  A stage is issued S-1 groups ahead;
+//   * the K loop walks 64-column groups through rings in LDS filled by
+//     direct global->LDS loads (no register staging): the tile's activation
+//     rows (fp16, already range-scaled), the lanes' packed codes and their
+//     scales.  Codes come as every lane's own window of one group (SC code
+//     stages, SC-1 groups ahead), or, for 8-bit codes with d = 2, as
+//     two-group chunks of 64 contiguous bytes per row; scales come four
+//     groups a row at a time, a quarter of the rows per step.  The loads per
+//     step are fixed, so every wait is a constant vmcnt;
 //   * the weights never exist as a dequantised tile: each lane decodes
 //     exactly its own v_mfma_f32_32x32x16_f16 B operand from its code window
 //     (codebook lookups in LDS, fp16 scale applied with packed multiplies),

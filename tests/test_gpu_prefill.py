@@ -80,6 +80,7 @@ def _run_moe(gate, up, down, x, ids, w):
     (96, 4, 4, 256, 128, 2, 10, 0, "bf16"),     # every expert routed by every token
     (40, 64, 2, 256, 128, 8, 9, 0, "bf16"),     # mostly empty experts
     (50, 8, 2, 384, 256, 2, 8, 0, "bf16"),      # 8-bit: 6 groups (gate, up), 4 (down)
+    (48, 8, 2, 256, 192, 4, 13, 2, "bf16"),     # 13-bit: gate, then up with SwiGLU
 ])
 def test_moe_prefill_small(T, E, k, H, I, d, bits, dead, dt):
     seed = 80 + T

@@ -639,75 +639,81 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
     // 8-bit codebooks: every raw entry copied into its row of copies: thread t
     // writes row k = t (NT >= 256 rows), chunk by chunk
     auto expand_cb = [&]() {
-        for (int k = tid; k < 256; k += NT) {
-            uint32_t ent[NPROJ][4];
-#pragma unroll
-            for (int p = 0; p < NPROJ; ++p) {
-                const bool ok = k * SH::ES < a.cb_bytes[p];
-                const char *src = raw + p * 256 * SH::ES + k * SH::ES;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    ent[p][i] = 0u;
-                if (ok) {
-                    if constexpr (D == 2) {
-                        ent[p][0] = *reinterpret_cast<const uint32_t *>(src);
-                    } else if constexpr (D == 4) {
-                        const uint2 q = *reinterpret_cast<const uint2 *>(src);
-                        ent[p][0] = q.x;
-                        ent[p][1] = q.y;
-                    } else {
-                        const uint4 q = *reinterpret_cast<const uint4 *>(src);
-                        ent[p][0] = q.x;
-                        ent[p][1] = q.y;
-                        ent[p][2] = q.z;
-                        ent[p][3] = q.w;
-                    }
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < 16; ++c) {
-                const int p = (NPROJ == 2) ? c / 8 : 0;
-                uint4 v;
+        // one 16-byte slot per thread and pass: the lanes of a wave fill the
+        // consecutive slots of four entries (1 KiB), so their stores fall on
+        // distinct banks; the 16 lanes of one entry read its raw bytes as a
+        // broadcast
+        for (int w = tid; w < 256 * 16; w += NT) {
+            const int k = w >> 4, c = w & 15;
+            const int p = (NPROJ == 2) ? (c >> 3) : 0;
+            const int lim = (p == 0) ? a.cb_bytes[0] : a.cb_bytes[NPROJ - 1];
+            const char *src = raw + p * 256 * SH::ES + k * SH::ES;
+            uint4 v = make_uint4(0u, 0u, 0u, 0u);
+            if (k * SH::ES < lim) {
                 if constexpr (D == 2) {
-                    v = make_uint4(ent[p][0], ent[p][0], ent[p][0], ent[p][0]);
+                    const uint32_t e = *reinterpret_cast<const uint32_t *>(src);
+                    v = make_uint4(e, e, e, e);
                 } else if constexpr (D == 4) {
-                    v = make_uint4(ent[p][0], ent[p][1], ent[p][0], ent[p][1]);
+                    const uint2 q = *reinterpret_cast<const uint2 *>(src);
+                    v = make_uint4(q.x, q.y, q.x, q.y);
                 } else {
-                    v = make_uint4(ent[p][0], ent[p][1], ent[p][2], ent[p][3]);
+                    v = *reinterpret_cast<const uint4 *>(src);
                 }
-                *reinterpret_cast<uint4 *>(smem + k * 256 + c * 16) = v;
             }
+            *reinterpret_cast<uint4 *>(smem + k * 256 + c * 16) = v;
         }
     };
 
     // ---- epilogue: lane holds D[8*(r/4) + 4*h + r%4][lane%32] of each block --------------
+    // Stores go through a buffer resource based at the tile's first output
+    // row and sized to end at row mlen: the range check drops the rows past
+    // the tile's end, and a lane past the last weight row takes an offset
+    // beyond any size, so no store needs a branch.  The row factors come four
+    // at a time from LDS.
+    static_assert(SH::KF_OFF % 16 == 0, "row factors are read as float4");
     auto store_tile = [&](auto NBc, auto &acc) {
         constexpr int NB = decltype(NBc)::value;
+        const uint32_t rs = (uint32_t)a.out_stride * 4u;   // bytes per output row
+        const uint32_t nrec = (uint32_t)mlen * rs;
+        const __amdgpu_buffer_rsrc_t ro =
+            __builtin_amdgcn_make_buffer_rsrc(a.out + (int64_t)m0 * a.out_stride, (short)0,
+                                              (int)nrec, 0x00020000);
+        const bool split = NPROJ == 1 && a.gate_in != nullptr;
+        __amdgpu_buffer_rsrc_t rg = ro;
+        if (split)
+            rg = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float *>(a.gate_in) + (int64_t)m0 * a.out_stride, (short)0,
+                (int)nrec, 0x00020000);
 #pragma unroll
         for (int nb = 0; nb < NN; ++nb) {
             const int n = nrow0 + 32 * nb;
-            const bool colok = n < a.rows;
+            const bool lv = NPROJ == 2 ? ((live >> nb & 1) && (live >> (NN + nb) & 1))
+                                       : (live >> nb & 1) != 0;
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
+                float4 f4[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    f4[q] = *reinterpret_cast<const float4 *>(kf + 32 * b + 8 * q + 4 * h);
+                const uint32_t vb =
+                    n < a.rows ? (uint32_t)(32 * b + 4 * h) * rs + (uint32_t)n * 4u : 0x80000000u;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int i = 32 * b + 8 * (r / 4) + 4 * h + (r % 4);
-                    if (!(colok && i < mlen))
-                        continue;
-                    const float f = kf[i];
-                    const int64_t o = (int64_t)(m0 + i) * a.out_stride + n;
+                    const float4 fq = f4[r / 4];
+                    const float f = (r % 4 == 0) ? fq.x : (r % 4 == 1) ? fq.y : (r % 4 == 2) ? fq.z : fq.w;
+                    const uint32_t off = vb + (uint32_t)(8 * (r / 4) + (r % 4)) * rs;
                     float v;
                     if constexpr (NPROJ == 2) {
-                        v = ((live >> nb & 1) && (live >> (NN + nb) & 1))
-                                ? silu_mul(acc[nb][b][r] * f, acc[NN + nb][b][r] * f)
-                                : 0.0f;
+                        v = silu_mul_fast(acc[nb][b][r] * f, acc[NN + nb][b][r] * f);
                     } else {
-                        if (a.gate_in)
-                            v = (live >> nb & 1) ? silu_mul(a.gate_in[o], acc[nb][b][r] * f) : 0.0f;
-                        else
-                            v = (live >> nb & 1) ? acc[nb][b][r] * f : 0.0f;
+                        v = acc[nb][b][r] * f;
+                        if (split)
+                            v = silu_mul_fast(__builtin_bit_cast(
+                                                  float, __builtin_amdgcn_raw_buffer_load_b32(rg, off, 0, 0)),
+                                              v);
                     }
-                    a.out[o] = v;
+                    v = lv ? v : 0.0f;
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ro, off, 0, 0);
                 }
             }
         }

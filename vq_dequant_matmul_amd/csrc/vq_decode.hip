@@ -124,7 +124,7 @@ static int cu_count()
 // 0; codebook 1 at 2^bits*d/2 dwords when that offset is at most 32 KiB (the
 // kernel then uses it as a constant), else right after codebook 0; the work
 // lists last.  Returns the LDS dwords.
-static int rows_args(const RowsLaunch &L, RowsArgs &a, int &gpl)
+static int rows_args(const RowsLaunch &L, RowsArgs &a, int &gpl, int iters)
 {
     const TensorDev &t0 = L.t[0];
     gpl = (t0.groups + 63) / 64;
@@ -145,7 +145,8 @@ static int rows_args(const RowsLaunch &L, RowsArgs &a, int &gpl)
     a.groups = t0.groups;
     a.wpr = t0.wpr;
     a.S_log2 = s_log2;
-    a.tile_rows = kWaves * kIters * rpw;
+    a.iters = iters;
+    a.tile_rows = kWaves * iters * rpw;
     a.tiles = (t0.rows + a.tile_rows - 1) / a.tile_rows;
     a.act = L.act;
     a.act_stride = L.act_stride;
@@ -175,10 +176,17 @@ hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream)
         return hipErrorInvalidValue;
     RowsArgs a;
     int gpl;
-    const size_t lds = (size_t)rows_args(L, a, gpl) * 4;
+    size_t lds = (size_t)rows_args(L, a, gpl, 2) * 4;
     const int P = L.ids ? L.n_slots : L.n_act;
     if (P == 0 || t0.rows == 0)
         return hipSuccess;
+    const int n_cu = cu_count();
+    // Two row passes per unit amortise a unit's setup; with bf16 activations
+    // and few units (about two per resident workgroup or fewer) one pass per
+    // unit spreads the work more evenly over the chip.  (fp32 activations,
+    // with their hi + lo terms, stay faster at two passes.)
+    if (L.act_f32 == 0 && (int64_t)P * a.tiles < (int64_t)kRowsOnePassUnitsPerCu * n_cu)
+        lds = (size_t)rows_args(L, a, gpl, 1) * 4;
     // a projection whose rows are all dead (skip-zero) stores nothing: every
     // output row it touches is exactly zero (for SwiGLU, silu(0)*u = 0 and
     // silu(g)*0 = 0 are written as +0.0)
@@ -187,7 +195,6 @@ hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream)
             return launch_fill_rows(L.out, P, t0.rows, L.out_stride, stream);
 
     const int64_t units = (int64_t)P * a.tiles;
-    const int n_cu = cu_count();
     switch (t0.d) {
     case 2: return rows_d<2>(t0.bits, a, gpl, L.nproj, L.act_f32, units, n_cu, lds, stream);
     case 4: return rows_d<4>(t0.bits, a, gpl, L.nproj, L.act_f32, units, n_cu, lds, stream);

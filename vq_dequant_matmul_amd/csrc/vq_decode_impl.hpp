@@ -38,6 +38,9 @@ namespace vq {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
+// a launch with bf16 activations and fewer units than this many per CU at
+// two row passes per unit takes one pass per unit
+constexpr int kRowsOnePassUnitsPerCu = 6;
 
 struct RowsArgs {
     const uint32_t *codes[2];
@@ -49,8 +52,9 @@ struct RowsArgs {
     int list_offset;    // dword offset of the work lists in LDS
     int rows, groups, wpr;
     int S_log2;         // lanes per row segment
-    int tile_rows;      // rows per work unit
+    int tile_rows;      // rows per work unit: waves * iters * rows per wave pass
     int tiles;          // tiles per expert
+    int iters;          // row passes of a wave per unit (1 or 2: the kernel's ITERS)
     const void *act;
     int64_t act_stride;
     float *out;
@@ -1147,16 +1151,15 @@ hipError_t mix_d(int bits, const MixArgs &a, size_t lds, hipStream_t s)
     VQ_BITS_SWITCH(bits, MixD<D>::template run, a, lds, s)
 }
 
-constexpr int kIters = 2;
 
 // The persistent grid is as many workgroups as can be resident at once
 // (occupancy of this instantiation at this LDS size, times the CU count),
 // capped by the number of work units.
-template <int D, int BITS, int GPL, int NPROJ, bool HL, bool F32>
+template <int D, int BITS, int GPL, int NPROJ, bool HL, bool F32, int ITERS>
 static hipError_t rows_launch(const RowsArgs &a, int64_t units, int n_cu, size_t lds_bytes,
                               hipStream_t stream)
 {
-    auto kern = k_rows<D, BITS, GPL, NPROJ, HL, F32, kIters>;
+    auto kern = k_rows<D, BITS, GPL, NPROJ, HL, F32, ITERS>;
     if (lds_bytes > 65536) {
         hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1178,17 +1181,27 @@ static hipError_t rows_launch(const RowsArgs &a, int64_t units, int n_cu, size_t
 // act: 0 bf16 activations; 1 fp32 ones, whose low bits ride along as a
 // second fp16 term; 2 fp32 ones rounded once to fp16 (one projection: the
 // down projection of h)
+template <int D, int BITS, int GPL, int NPROJ, int ITERS>
+static hipError_t rows_iters(const RowsArgs &a, int act, int64_t units, int n_cu, size_t lds,
+                             hipStream_t s)
+{
+    if constexpr (NPROJ == 1) {
+        if (act == 2)
+            return rows_launch<D, BITS, GPL, NPROJ, false, true, ITERS>(a, units, n_cu, lds, s);
+    }
+    if (act != 0)
+        return rows_launch<D, BITS, GPL, NPROJ, true, true, ITERS>(a, units, n_cu, lds, s);
+    return rows_launch<D, BITS, GPL, NPROJ, false, false, ITERS>(a, units, n_cu, lds, s);
+}
+
+// one or two row passes per unit (a.iters)
 template <int D, int BITS, int GPL, int NPROJ>
 static hipError_t rows_act(const RowsArgs &a, int act, int64_t units, int n_cu, size_t lds,
                            hipStream_t s)
 {
-    if constexpr (NPROJ == 1) {
-        if (act == 2)
-            return rows_launch<D, BITS, GPL, NPROJ, false, true>(a, units, n_cu, lds, s);
-    }
-    if (act != 0)
-        return rows_launch<D, BITS, GPL, NPROJ, true, true>(a, units, n_cu, lds, s);
-    return rows_launch<D, BITS, GPL, NPROJ, false, false>(a, units, n_cu, lds, s);
+    if (a.iters == 1)
+        return rows_iters<D, BITS, GPL, NPROJ, 1>(a, act, units, n_cu, lds, s);
+    return rows_iters<D, BITS, GPL, NPROJ, 2>(a, act, units, n_cu, lds, s);
 }
 
 template <int D, int BITS>

@@ -256,3 +256,29 @@ def test_moe_prefill_all_rows_dead(which):
     assert np.all(ref == 0) and np.all(y == 0)
     if which == "down":
         assert np.all(y.view(np.uint32) == 0)
+
+
+def test_moe_prefill_down_magnitudes():
+    """Down rows whose scales span 2^-16 .. 2^12 inside every 64-column
+    chunk, and experts 2^10 apart: the down projection's fp16 outputs carry
+    one exponent per (tile, 64 columns), so each chunk's large columns set
+    it and each expert's tile has its own; the combined output still matches
+    the oracle."""
+    T, E, k, H, I = 160, 8, 2, 512, 256
+    gate, up, down = _layer(99, E, H, I, 2, 8, (0, 0, 5))
+    rng = np.random.default_rng(99)
+    sc = down.scales.view(np.float16).astype(np.float64)
+    row_exp = rng.integers(-16, 13, size=(sc.shape[0], 1))
+    expert_of = np.repeat(np.arange(E), H)
+    if down.row_map is not None:
+        stored = down.row_map >= 0
+        owner = np.empty(sc.shape[0], dtype=np.int64)
+        owner[down.row_map[stored]] = expert_of[stored]
+    else:
+        owner = expert_of
+    exp_shift = np.where(owner % 2 == 0, 0, -10)[:, None]
+    down.scales = synth.to_half_bits(sc * np.exp2(row_exp + exp_shift))
+    x = synth.make_x(99, 4, T, H, "bf16")
+    ids, w = synth.make_routes(99, 5, T, E, k)
+    y = _run_moe(gate, up, down, x, ids, w)
+    check_close(y, oracle.moe_ffn(gate, up, down, x, ids, w), "down magnitudes")

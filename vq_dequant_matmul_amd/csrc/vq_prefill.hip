@@ -22,7 +22,12 @@ VQ_DECL_GEMM(8)
 #undef VQ_DECL_GEMM
 
 constexpr int kRouteThreads = 1024;
-constexpr int kRouteBatch = 8;   // ids per thread loaded together
+// ids per thread loaded together; a batch of up to kRouteThreads *
+// kRouteBatch pairs stays in registers from the count to the scatter, so
+// the single routing workgroup waits for the ids once instead of once per
+// pass and batch (the rest of the chip is streaming activations meanwhile,
+// so each round trip is long)
+constexpr int kRouteBatch = 48;
 constexpr int kMaxRouteExperts = 4096;
 
 // Exclusive scan of v[0..n) in place (n <= 4 * kRouteThreads); returns the
@@ -112,9 +117,11 @@ __device__ __forceinline__ void route_body(const int32_t *__restrict__ ids, int 
     }
     __syncthreads();
     // the ids are read kRouteBatch per thread at a time, so their loads are
-    // in flight together instead of one round trip per id
+    // in flight together instead of one round trip per id; a single batch
+    // is kept for the scatter below
+    const bool held = P <= kRouteThreads * kRouteBatch;
+    int id[kRouteBatch];
     for (int q0 = 0; q0 < P; q0 += kRouteThreads * kRouteBatch) {
-        int id[kRouteBatch];
 #pragma unroll
         for (int k = 0; k < kRouteBatch; ++k) {
             const int q = q0 + k * kRouteThreads + tid;
@@ -135,11 +142,12 @@ __device__ __forceinline__ void route_body(const int32_t *__restrict__ ids, int 
     if (tid == 0)
         offs[E] = total;
     for (int q0 = 0; q0 < P; q0 += kRouteThreads * kRouteBatch) {
-        int id[kRouteBatch];
+        if (!held) {
 #pragma unroll
-        for (int k = 0; k < kRouteBatch; ++k) {
-            const int q = q0 + k * kRouteThreads + tid;
-            id[k] = q < P ? ids[q] : 0;
+            for (int k = 0; k < kRouteBatch; ++k) {
+                const int q = q0 + k * kRouteThreads + tid;
+                id[k] = q < P ? ids[q] : 0;
+            }
         }
 #pragma unroll
         for (int k = 0; k < kRouteBatch; ++k) {
@@ -275,30 +283,40 @@ __global__ __launch_bounds__(kRouteThreads) void k_route_rowscale(
     rowscale_row(x, f32, rows, cols, (int64_t)cols, out, k, row);
 }
 
-// y[t][c] = sum over slots s (in order) of w[t][s] * z[pos[t*k + s]][c].
-__global__ __launch_bounds__(256) void k_combine_perm(const float *__restrict__ z,
-                                                      const int32_t *__restrict__ pos,
-                                                      const float *__restrict__ w, int n_tok,
-                                                      int top_k, int hidden, float *__restrict__ y)
+// y[t][c] = sum over slots s (in order) of w[t][s] * z[pos[t*k + s]][c], with
+// z the grouped GEMM's fp16 outputs and their exponents:
+// z[p][c] = zh[p][c] * 2^-(ze[p][c/64] + hk[p]), hk the exponents of the
+// down projection's activation rows.  Eight columns per thread.
+__global__ __launch_bounds__(256) void k_combine_perm_h(const f16 *__restrict__ zh,
+                                                        const int8_t *__restrict__ ze,
+                                                        const int32_t *__restrict__ hk,
+                                                        const int32_t *__restrict__ pos,
+                                                        const float *__restrict__ w, int n_tok,
+                                                        int top_k, int hidden,
+                                                        float *__restrict__ y)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t n4 = (int64_t)n_tok * hidden / 4;
-    if (i >= n4)
+    const int64_t n8 = (int64_t)n_tok * hidden / 8;
+    if (i >= n8)
         return;
-    const int64_t t = (i * 4) / hidden;
-    const int64_t c = (i * 4) % hidden;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
+    const int64_t t = (i * 8) / hidden;
+    const int c = (int)((i * 8) % hidden);
+    const int nch = hidden >> 6;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
     for (int s = 0; s < top_k; ++s) {
         const float ws = w[t * top_k + s];
-        const float4 v =
-            *reinterpret_cast<const float4 *>(z + (int64_t)pos[t * top_k + s] * hidden + c);
-        acc.x += ws * v.x;
-        acc.y += ws * v.y;
-        acc.z += ws * v.z;
-        acc.w += ws * v.w;
+        const int64_t p = pos[t * top_k + s];
+        const int ex = (int)ze[p * nch + (c >> 6)] + hk[p];
+        union { uint4 u; f16 v[8]; } q;
+        q.u = *reinterpret_cast<const uint4 *>(zh + p * hidden + c);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc[j] += ws * ldexpf((float)q.v[j], -ex);
     }
-    *reinterpret_cast<float4 *>(y + t * hidden + c) = acc;
+    float4 *o = reinterpret_cast<float4 *>(y + t * hidden + c);
+    o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
 }
 
 // Zero fill (used when every row of a tensor is dead: the product is zero).
@@ -380,7 +398,8 @@ static hipError_t launch_gemm(const TensorDev &t0, const TensorDev *t1, int mb, 
                               int act_stride, const int32_t *act_k, const int32_t *perm,
                               int act_div, const int32_t *tiles, const int32_t *n_tiles,
                               int64_t tile_cap, float *out, int64_t out_stride,
-                              const float *gate_in, const int32_t *gate_map, hipStream_t stream)
+                              const float *gate_in, const int32_t *gate_map, hipStream_t stream,
+                              f16 *out_h = nullptr, int8_t *out_e = nullptr)
 {
     GemmArgs a = {};
     const TensorDev *ts[2] = {&t0, t1};
@@ -407,6 +426,10 @@ static hipError_t launch_gemm(const TensorDev &t0, const TensorDev *t1, int mb, 
     a.gate_in = gate_in;
     a.out = out;
     a.out_stride = out_stride;
+    a.out_h = out_h;
+    a.out_e = out_e;
+    if (out_e && (t1 || out_stride % 64 != 0 || out_stride != t0.rows))
+        return hipErrorInvalidValue;
     if (tile_cap > 0x7fffffff)
         return hipErrorInvalidValue;
     switch (t0.d) {
@@ -487,7 +510,7 @@ hipError_t launch_expert_gemm(const TensorDev &t, int n_x_rows, const void *x, i
 // ---- vq_moe_ffn, many tokens ---------------------------------------------------
 
 struct FfnWs {
-    size_t offs, perm, pos, tiles, n_tiles, xs, xk, g, h, hs, hk, z, total;
+    size_t offs, perm, pos, tiles, n_tiles, xs, xk, g, h, hs, hk, zh, ze, total;
     int mb;
     bool fused;
     int64_t cap;
@@ -517,7 +540,8 @@ static FfnWs ffn_ws(const TensorDev &g, const TensorDev &dn, int n_tok, int top_
     w.h = take((size_t)P * g.rows * 4);
     w.hs = take((size_t)P * g.rows * 2);
     w.hk = take((size_t)P * 4);
-    w.z = take((size_t)P * dn.rows * 4);
+    w.zh = take((size_t)P * dn.rows * 2);
+    w.ze = take((size_t)P * (dn.rows / 64));
     w.total = o;
     return w;
 }
@@ -549,7 +573,8 @@ hipError_t launch_moe_prefill(const TensorDev &g, const TensorDev &u, const Tens
     float *h = reinterpret_cast<float *>(base + w.h);
     f16 *hs = reinterpret_cast<f16 *>(base + w.hs);
     int32_t *hk = reinterpret_cast<int32_t *>(base + w.hk);
-    float *z = reinterpret_cast<float *>(base + w.z);
+    f16 *zh = reinterpret_cast<f16 *>(base + w.zh);
+    int8_t *ze = reinterpret_cast<int8_t *>(base + w.ze);
     const int P = n_tok * top_k;
     const int E = g.n_experts;
 
@@ -584,13 +609,15 @@ hipError_t launch_moe_prefill(const TensorDev &g, const TensorDev &u, const Tens
         return e;
     if ((e = launch_rowscale(h, 1, P, g.rows, hs, hk, stream)) != hipSuccess)
         return e;
-    e = launch_gemm(dn, nullptr, w.mb, hs, g.rows, hk, nullptr, 1, tiles, n_tiles, w.cap, z,
-                    dn.rows, nullptr, nullptr, stream);
+    // the down projection's outputs in fp16 with exponents per (tile, 64
+    // columns): half the bytes of fp32 written here and read by the combine
+    e = launch_gemm(dn, nullptr, w.mb, hs, g.rows, hk, nullptr, 1, tiles, n_tiles, w.cap, nullptr,
+                    dn.rows, nullptr, nullptr, stream, zh, ze);
     if (e != hipSuccess)
         return e;
-    const int64_t n4 = (int64_t)n_tok * dn.rows / 4;
-    hipLaunchKernelGGL(k_combine_perm, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, stream, z,
-                       pos, wts, n_tok, top_k, dn.rows, y);
+    const int64_t n8 = (int64_t)n_tok * dn.rows / 8;
+    hipLaunchKernelGGL(k_combine_perm_h, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
+                       zh, ze, hk, pos, wts, n_tok, top_k, dn.rows, y);
     return hipGetLastError();
 }
 

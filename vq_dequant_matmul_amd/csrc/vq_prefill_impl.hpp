@@ -158,6 +158,11 @@ struct GemmArgs {
     const float *gate_in;          // split SwiGLU: gate outputs for this up projection
     float *out;
     int64_t out_stride;
+    // one projection only: fp16 outputs in out_h (row stride out_stride, a
+    // multiple of 64) with one power-of-two exponent per (tile, 64-column
+    // chunk) repeated into out_e[row][chunk] (then out is unused)
+    f16 *out_h;
+    int8_t *out_e;
 };
 
 // Shape of one launch.  A workgroup has WAVES waves; each wave owns NN blocks
@@ -719,6 +724,76 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
         }
     };
 
+    // fp16 outputs (one projection; the routed FFN's down projection, whose
+    // rows a combine reads back): per 64-column chunk of the wave (blocks 2c
+    // and 2c + 1) every row of the tile is scaled by the one power of two 2^E
+    // that puts the chunk's largest magnitude over the tile in [2^14, 2^15),
+    // rounded to fp16, and E goes to out_e[row][chunk].  The activation rows
+    // were range-scaled one by one, so the tile's rows have like magnitudes
+    // and each value keeps fp16's relative precision; the row factor is not
+    // applied here (a reader takes 2^-(E + k) with the row's exponent k).
+    // Dead weight rows and lanes past the last weight row give +0.0.
+    auto store_tile_h = [&](auto NBc, auto &acc) {
+        constexpr int NB = decltype(NBc)::value;
+        static_assert(NPROJ == 1 && NN % 2 == 0, "chunks are pairs of blocks of one projection");
+        const int nch = (int)(a.out_stride >> 6);
+        const uint32_t rs = (uint32_t)a.out_stride * 2u;   // bytes per output row
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            a.out_h + (int64_t)m0 * a.out_stride, (short)0, (int)((uint32_t)mlen * rs), 0x00020000);
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            a.out_e + (int64_t)m0 * nch, (short)0, mlen * nch, 0x00020000);
+#pragma unroll
+        for (int c = 0; c < NN / 2; ++c) {
+            const int n0 = nrow0 + 64 * c, n1 = n0 + 32;
+            // the chunk's first column (uniform); the row count is a multiple
+            // of 64, so a chunk is wholly inside or wholly past the end
+            const int cb = __builtin_amdgcn_readfirstlane(n0 - (lane & 31));
+            if (cb >= a.rows)
+                continue;
+            const bool l0 = (live >> (2 * c) & 1) != 0, l1 = (live >> (2 * c + 1) & 1) != 0;
+            float mx = 0.0f;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    mx = fmaxf(mx, fmaxf(l0 ? fabsf(acc[2 * c][b][r]) : 0.0f,
+                                         l1 ? fabsf(acc[2 * c + 1][b][r]) : 0.0f));
+            mx = segment_max16_dpp(mx);
+            {
+                const uint32_t u = __float_as_uint(mx);
+                const auto q = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+                mx = fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+                const auto q2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                                 __float_as_uint(mx), false, false);
+                mx = fmaxf(__uint_as_float(q2[0]), __uint_as_float(q2[1]));
+            }
+            const int ex = range_exponent(mx);
+            const float up = ldexpf(1.0f, ex);
+            const int ch = cb >> 6;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const uint32_t v0 = n0 < a.rows ? (uint32_t)(32 * b + 4 * h) * rs + (uint32_t)n0 * 2u
+                                                : 0x80000000u;
+                const uint32_t v1 = n1 < a.rows ? (uint32_t)(32 * b + 4 * h) * rs + (uint32_t)n1 * 2u
+                                                : 0x80000000u;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const uint32_t off = (uint32_t)(8 * (r / 4) + (r % 4)) * rs;
+                    const f16 y0 = (f16)(l0 ? acc[2 * c][b][r] * up : 0.0f);
+                    const f16 y1 = (f16)(l1 ? acc[2 * c + 1][b][r] * up : 0.0f);
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, y0), ro,
+                                                          v0 + off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, y1), ro,
+                                                          v1 + off, 0, 0);
+                }
+                // the exponent of tile row 32b + lane (lanes 0..31)
+                const uint32_t vx = lane < 32 ? (uint32_t)(32 * b + lane) * (uint32_t)nch + (uint32_t)ch
+                                              : 0x80000000u;
+                __builtin_amdgcn_raw_buffer_store_b8((unsigned char)(signed char)ex, rx, vx, 0, 0);
+            }
+        }
+    };
+
     // ---- the K loop for a tile of NB blocks ---------------------------------------------
     // Step g reads the activation rows of group g from activation stage g % SA
     // and the code windows of group g + 1 from code stage (g + 1) % SC.  It
@@ -870,6 +945,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
         // nothing may land in LDS after the workgroup ends
         wait_vm<0>();
 
+        if constexpr (NPROJ == 1 && NN % 2 == 0) {
+            if (a.out_e) {
+                store_tile_h(NBc, acc);
+                return;
+            }
+        }
         store_tile(NBc, acc);
     };
 
@@ -1059,6 +1140,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
         // nothing may land in LDS after the workgroup ends
         wait_vm<0>();
 
+        if constexpr (NPROJ == 1 && NN % 2 == 0) {
+            if (a.out_e) {
+                store_tile_h(NBc, acc);
+                return;
+            }
+        }
         store_tile(NBc, acc);
     };
 

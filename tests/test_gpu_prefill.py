@@ -35,6 +35,11 @@ GEMM_CASES = [
     (4, 13, 130, 384, 2, [17, 60], "bf16", 3),
     (2, 8, 300, 448, 3, [40, 100, 5], "bf16", 9),          # 8-bit, 7 groups a row
     (2, 8, 520, 256, 2, [64, 97], "f32", 3),               # 8-bit, 4 groups, ragged rows
+    # 8-bit d2 blocks near 100 rows: 128-row tiles in the chunk-only LDS layout
+    (2, 8, 600, 512, 4, [100, 128, 97, 33], "bf16", 11),
+    (2, 8, 1024, 1024, 3, [120, 88, 101], "bf16", 0),
+    # the same block sizes with 7 groups a row: no chunks, 96-row tiles
+    (2, 8, 300, 448, 4, [100, 128, 97, 33], "bf16", 0),
 ]
 
 
@@ -81,6 +86,7 @@ def _run_moe(gate, up, down, x, ids, w):
     (40, 64, 2, 256, 128, 8, 9, 0, "bf16"),     # mostly empty experts
     (50, 8, 2, 384, 256, 2, 8, 0, "bf16"),      # 8-bit: 6 groups (gate, up), 4 (down)
     (48, 8, 2, 256, 192, 4, 13, 2, "bf16"),     # 13-bit: gate, then up with SwiGLU
+    (200, 16, 8, 512, 256, 2, 8, 7, "bf16"),    # 8-bit, ~100 rows an expert: 128-row tiles
 ])
 def test_moe_prefill_small(T, E, k, H, I, d, bits, dead, dt):
     seed = 80 + T

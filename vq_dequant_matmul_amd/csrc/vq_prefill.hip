@@ -102,10 +102,11 @@ __device__ void build_tiles(const int *cnt, const int *offs, int *toff, int E, i
         *n_tiles = total;
 }
 
-// Route grouping for the MoE FFN: pairs q = t*top_k + s by expert.
+// Route grouping for the MoE FFN: pairs q = t*top_k + s by expert; pos[q]
+// receives the pair's grouped position (its inverse is k_invert_pos).
 __device__ __forceinline__ void route_body(const int32_t *__restrict__ ids, int P, int E, int mt,
-                                           int32_t *__restrict__ offs, int32_t *__restrict__ perm,
-                                           int32_t *__restrict__ pos, int32_t *__restrict__ tiles,
+                                           int32_t *__restrict__ offs, int32_t *__restrict__ pos,
+                                           int32_t *__restrict__ tiles,
                                            int32_t *__restrict__ n_tiles)
 {
     extern __shared__ int s[];
@@ -154,7 +155,6 @@ __device__ __forceinline__ void route_body(const int32_t *__restrict__ ids, int 
             const int q = q0 + k * kRouteThreads + tid;
             if (q < P) {
                 const int p = base[id[k]] + atomicAdd(&fill[id[k]], 1);
-                perm[p] = q;
                 pos[q] = p;
             }
         }
@@ -266,17 +266,29 @@ __global__ __launch_bounds__(256) void k_rowscale(const void *__restrict__ x, in
     rowscale_row(x, f32, rows, cols, stride, out, k, blockIdx.x * 4 + (threadIdx.x >> 6));
 }
 
+// perm[pos[q]] = q: the grouped order's source pairs.  The routing
+// workgroup writes pos only (in pair order, so its stores are coalesced);
+// this scatter of one dword per pair to random lines is spread over many
+// workgroups instead of queueing behind one CU's memory pipeline.
+__global__ __launch_bounds__(256) void k_invert_pos(const int32_t *__restrict__ pos, int P,
+                                                    int32_t *__restrict__ perm)
+{
+    const int q = blockIdx.x * 256 + threadIdx.x;
+    if (q < P)
+        perm[pos[q]] = q;
+}
+
 // The routing (workgroup 0) and the activation rows' scaling (the other
 // workgroups, kRouteThreads / 64 rows each) in one launch: they are
 // independent, and the routing alone leaves the rest of the chip idle.
 __global__ __launch_bounds__(kRouteThreads) void k_route_rowscale(
     const int32_t *__restrict__ ids, int P, int E, int mt, int32_t *__restrict__ offs,
-    int32_t *__restrict__ perm, int32_t *__restrict__ pos, int32_t *__restrict__ tiles,
+    int32_t *__restrict__ pos, int32_t *__restrict__ tiles,
     int32_t *__restrict__ n_tiles, const void *__restrict__ x, int f32, int rows, int cols,
     f16 *__restrict__ out, int32_t *__restrict__ k)
 {
     if (blockIdx.x == 0) {
-        route_body(ids, P, E, mt, offs, perm, pos, tiles, n_tiles);
+        route_body(ids, P, E, mt, offs, pos, tiles, n_tiles);
         return;
     }
     const int row = (blockIdx.x - 1) * (kRouteThreads / 64) + (threadIdx.x >> 6);
@@ -357,11 +369,11 @@ static size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 // the down projection.
 static int mb_level(const TensorDev &t, bool ffn, const TensorDev *dn, int mb)
 {
-    int lv = gemm_fit(t.d, t.bits, ffn ? 2 : 1, mb, t.rows);
+    int lv = gemm_fit(t.d, t.bits, ffn ? 2 : 1, mb, t.rows, t.groups);
     if (ffn && lv == 0)
-        lv = gemm_fit(t.d, t.bits, 1, mb, t.rows);
+        lv = gemm_fit(t.d, t.bits, 1, mb, t.rows, t.groups);
     if (dn)
-        lv = std::min(lv, gemm_fit(dn->d, dn->bits, 1, mb, dn->rows));
+        lv = std::min(lv, gemm_fit(dn->d, dn->bits, 1, mb, dn->rows, dn->groups));
     return lv;
 }
 
@@ -391,7 +403,7 @@ static int64_t max_tiles(int64_t rows, int E, int mt)
 // gate and up in one launch unless their codebooks leave no room for the ring
 static bool fused_gate_up(const TensorDev &g, int mb)
 {
-    return gemm_fits(g.d, g.bits, 2, mb, g.rows);
+    return gemm_fits(g.d, g.bits, 2, mb, g.rows, g.groups);
 }
 
 static hipError_t launch_gemm(const TensorDev &t0, const TensorDev *t1, int mb, const f16 *act,
@@ -478,7 +490,7 @@ hipError_t launch_expert_gemm(const TensorDev &t, int n_x_rows, const void *x, i
     if (t.n_experts > kMaxRouteExperts)
         return hipErrorNotSupported;
     const GemmWs w = gemm_ws(t, n_x_rows);
-    if (!gemm_fits(t.d, t.bits, 1, w.mb, t.rows))
+    if (!gemm_fits(t.d, t.bits, 1, w.mb, t.rows, t.groups))
         return hipErrorNotSupported;
     char *base = static_cast<char *>(ws);
     int32_t *tiles = reinterpret_cast<int32_t *>(base + w.tiles);
@@ -559,7 +571,8 @@ hipError_t launch_moe_prefill(const TensorDev &g, const TensorDev &u, const Tens
     if (g.n_experts > kMaxRouteExperts)
         return hipErrorNotSupported;
     const FfnWs w = ffn_ws(g, dn, n_tok, top_k);
-    if (!gemm_fits(g.d, g.bits, 1, w.mb, g.rows) || !gemm_fits(dn.d, dn.bits, 1, w.mb, dn.rows))
+    if (!gemm_fits(g.d, g.bits, 1, w.mb, g.rows, g.groups) ||
+        !gemm_fits(dn.d, dn.bits, 1, w.mb, dn.rows, dn.groups))
         return hipErrorNotSupported;
     char *base = static_cast<char *>(ws);
     int32_t *offs = reinterpret_cast<int32_t *>(base + w.offs);
@@ -582,10 +595,14 @@ hipError_t launch_moe_prefill(const TensorDev &g, const TensorDev &u, const Tens
     const size_t lds_r = (size_t)(4 * E + 17) * 4;
     const int rs_wgs = (n_tok + kRouteThreads / 64 - 1) / (kRouteThreads / 64);
     hipLaunchKernelGGL(k_route_rowscale, dim3((unsigned)(1 + rs_wgs)), dim3(kRouteThreads), lds_r,
-                       stream, ids, P, E, 32 * w.mb, offs, perm, pos, tiles, n_tiles, x, x_f32,
+                       stream, ids, P, E, 32 * w.mb, offs, pos, tiles, n_tiles, x, x_f32,
                        n_tok, g.cols, xs, xk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_invert_pos, dim3((unsigned)((P + 255) / 256)), dim3(256), 0, stream, pos,
+                       P, perm);
+    if ((e = hipGetLastError()) != hipSuccess)
         return e;
     if (g.n_stored == 0 || u.n_stored == 0 || dn.n_stored == 0)
         return launch_zero(y, (int64_t)n_tok * dn.rows, stream);

@@ -213,34 +213,6 @@ struct GemmShape {
     static constexpr int CB_BYTES = BANKED ? 256 * 256 : NPROJ * CB_SLOT;
     static constexpr int KF_OFF = CB_BYTES;                     // row factors of the tile
     static constexpr int FIXED = KF_OFF + 32 * MB * 4;
-    // Ring depths: code windows SC stages (loaded SC - 1 groups ahead), the
-    // activation rows SA stages (SA - 1 ahead); the deepest pair that fits,
-    // with SA >= SC - 1
-    static constexpr bool fits(int sc, int sa)
-    {
-        return FIXED + sreg(sc) + sc * C_BYTES + sa * A_BYTES <= kLdsBudget;
-    }
-    static constexpr int SC = fits(5, 4) ? 5 : (fits(4, 3) ? 4 : 3);
-    static constexpr int SA = fits(5, 4) ? 4 : (fits(4, 3) ? 3 : (fits(3, 3) ? 3 : 2));
-    // with fewer stages the top of every step waits for all loads of the
-    // previous one (correct, but nothing stays in flight across steps)
-    static constexpr bool DEEP = fits(3, 3);
-    static constexpr int SLOTS = slots(SC);
-    static constexpr int SW = sw(SC);
-    static constexpr int SREG = sreg(SC);
-    static constexpr int SRING = FIXED;
-    static constexpr int CRING = FIXED + SREG;
-    static constexpr int ARING = CRING + SC * C_BYTES;
-    static constexpr int LDS = ARING + SA * A_BYTES;
-    // the 8-bit codebooks arrive through the last code stage before they are
-    // copied out
-    static constexpr bool FITS =
-        ACC_OK && fits(SC, SA) && (!BANKED || NPROJ * 256 * ES <= C_BYTES);
-    // vmcnt at the top of step g: activation rows of group g and the code
-    // windows of group g + 1 have landed (every earlier step issued NOPS)
-    static constexpr int W_TOP = ((SA - 2) * NOPS < NOPS_A + (SC - 3) * NOPS)
-                                     ? (SA - 2) * NOPS : NOPS_A + (SC - 3) * NOPS;
-    static_assert(SC * 128 <= SW, "one scale dword per row and code stage");
     // Two-group code chunks (8-bit codes, d = 2, a multiple of four groups
     // per row): per (projection, block) and wave one slot of 32 rows x 64
     // bytes (groups 2j, 2j+1) and a three-slot scale ring, both inside the
@@ -251,9 +223,51 @@ struct GemmShape {
     static constexpr int CH_SLOT = 2048;
     static constexpr int CH_SW = 768;
     static constexpr int CH_CODES = NPB * WAVES * CH_SLOT;
-    static constexpr bool CHUNK = BANKED && D == 2 && SA >= 3 &&
-                                  CH_CODES + NPB * WAVES * CH_SW <= SC * C_BYTES &&
-                                  NPROJ * 256 * ES <= SREG;
+    static constexpr int CH_REGION = CH_CODES + NPB * WAVES * CH_SW;
+    static constexpr int CH_RAW = NPROJ * 256 * ES;             // raw 8-bit codebooks
+    // Ring depths: code windows SC stages (loaded SC - 1 groups ahead), the
+    // activation rows SA stages (SA - 1 ahead); the deepest pair that fits,
+    // with SA >= SC - 1
+    static constexpr bool fits(int sc, int sa)
+    {
+        return FIXED + sreg(sc) + sc * C_BYTES + sa * A_BYTES <= kLdsBudget;
+    }
+    // A layout for the chunk schedule alone (CHONLY), used where the general
+    // one cannot keep loads in flight across steps (tall tiles): after the
+    // codebooks and row factors only the raw codebooks, the chunk slots with
+    // their scale ring, and the activation stages.  Such a launch needs a
+    // multiple of four groups per row (the host checks).
+    static constexpr bool fits_ch(int sa)
+    {
+        return FIXED + CH_RAW + CH_REGION + sa * A_BYTES <= kLdsBudget;
+    }
+    static constexpr bool CHONLY = BANKED && D == 2 && !fits(3, 3) && fits_ch(3);
+    static constexpr int SC = CHONLY ? 3 : (fits(5, 4) ? 5 : (fits(4, 3) ? 4 : 3));
+    static constexpr int SA = CHONLY ? (fits_ch(4) ? 4 : 3)
+                                     : (fits(5, 4) ? 4 : (fits(4, 3) ? 3 : (fits(3, 3) ? 3 : 2)));
+    // with fewer stages the top of every step waits for all loads of the
+    // previous one (correct, but nothing stays in flight across steps)
+    static constexpr bool DEEP = CHONLY || fits(3, 3);
+    static constexpr int SLOTS = slots(SC);
+    static constexpr int SW = sw(SC);
+    static constexpr int SREG = CHONLY ? CH_RAW : sreg(SC);
+    static constexpr int SRING = FIXED;
+    static constexpr int CRING = FIXED + SREG;
+    static constexpr int ARING = CRING + (CHONLY ? CH_REGION : SC * C_BYTES);
+    static constexpr int LDS = ARING + SA * A_BYTES;
+    // the 8-bit codebooks arrive through the last code stage before they are
+    // copied out (through the scale region with chunks)
+    static constexpr bool FITS =
+        ACC_OK && (CHONLY ? fits_ch(SA)
+                          : (fits(SC, SA) && (!BANKED || NPROJ * 256 * ES <= C_BYTES)));
+    // vmcnt at the top of step g: activation rows of group g and the code
+    // windows of group g + 1 have landed (every earlier step issued NOPS)
+    static constexpr int W_TOP = ((SA - 2) * NOPS < NOPS_A + (SC - 3) * NOPS)
+                                     ? (SA - 2) * NOPS : NOPS_A + (SC - 3) * NOPS;
+    static_assert(SC * 128 <= SW, "one scale dword per row and code stage");
+    static constexpr bool CHUNK = CHONLY || (BANKED && D == 2 && SA >= 3 &&
+                                             CH_REGION <= SC * C_BYTES && CH_RAW <= SREG);
+    static_assert(!CHONLY || (SA >= 3 && CH_RAW <= SREG), "chunk-only layout");
     static constexpr int CH_E = NPB + NDMA_A;
     static constexpr int CH_O = 3 * NPB + NDMA_A;
     static_assert(CH_O < 64, "vmcnt out of range");
@@ -1153,7 +1167,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
     static_for<MB>([&](auto I) {
         constexpr int nb = decltype(I)::value + 1;
         if (nblk == nb) {
-            if constexpr (SH::CHUNK) {
+            if constexpr (SH::CHONLY) {
+                if (chunk)   // always: the host launches this layout only then
+                    body_ch(std::integral_constant<int, nb>{});
+            } else if constexpr (SH::CHUNK) {
                 if (chunk)
                     body_ch(std::integral_constant<int, nb>{});
                 else
@@ -1194,6 +1211,8 @@ static hipError_t gemm_launch(GemmArgs a, int tile_cap, hipStream_t stream)
     if constexpr (!SH::FITS) {
         return hipErrorOutOfMemory;
     } else {
+        if (SH::CHONLY && (a.groups & 3) != 0)
+            return hipErrorInvalidValue;   // the chunk-only layout needs four groups a step
         const void *kern = reinterpret_cast<const void *>(k_gemm<D, BITS, NPROJ, MB, NN, WAVES>);
         a.n_ntiles = (a.rows + SH::WG_ROWS - 1) / SH::WG_ROWS;
         const int64_t wgs = (int64_t)((tile_cap + 7) / 8) * 8 * a.n_ntiles;
@@ -1235,9 +1254,10 @@ struct GemmD {
 };
 
 // Host side of GemmShape: 0 = does not fit, 1 = fits, 2 = fits with loads in
-// flight across steps.
+// flight across steps.  The chunk-only layout takes rows of a multiple of
+// four groups only.
 template <int D, int BITS, int NPROJ, int NN>
-inline int gemm_fit_level(int mb)
+inline int gemm_fit_level(int mb, int groups)
 {
     constexpr int W = gemm_waves(BITS);
     using S2 = GemmShape<D, BITS, NPROJ, 2, NN, W>;
@@ -1245,17 +1265,21 @@ inline int gemm_fit_level(int mb)
     using S4 = GemmShape<D, BITS, NPROJ, 4, NN, W>;
     const bool f = mb == 2 ? S2::FITS : (mb == 3 ? S3::FITS : S4::FITS);
     const bool d = mb == 2 ? S2::DEEP : (mb == 3 ? S3::DEEP : S4::DEEP);
+    const bool co = mb == 2 ? S2::CHONLY : (mb == 3 ? S3::CHONLY : S4::CHONLY);
+    if (co && (groups & 3) != 0)
+        return 0;
     return f ? (d ? 2 : 1) : 0;
 }
 
 template <int D, int BITS>
-inline int gemm_fit_db(int nproj, int mb, int rows)
+inline int gemm_fit_db(int nproj, int mb, int rows, int groups)
 {
     constexpr int W = gemm_waves(BITS);
     if constexpr (W == 8) {
         if (mb > 4)
             return 0;
-        return nproj == 2 ? gemm_fit_level<D, BITS, 2, 1>(mb) : gemm_fit_level<D, BITS, 1, 2>(mb);
+        return nproj == 2 ? gemm_fit_level<D, BITS, 2, 1>(mb, groups)
+                          : gemm_fit_level<D, BITS, 1, 2>(mb, groups);
     } else {
         if (mb == 5) {
             using S = GemmShape<D, BITS, 2, 5, 1, W>;
@@ -1265,35 +1289,37 @@ inline int gemm_fit_db(int nproj, int mb, int rows)
             return f ? (d ? 2 : 1) : 0;
         }
         if (nproj == 2)
-            return gemm_fit_level<D, BITS, 2, 2>(mb);
-        return gemm_nn(1, rows) == 4 ? gemm_fit_level<D, BITS, 1, 4>(mb)
-                                     : gemm_fit_level<D, BITS, 1, 2>(mb);
+            return gemm_fit_level<D, BITS, 2, 2>(mb, groups);
+        return gemm_nn(1, rows) == 4 ? gemm_fit_level<D, BITS, 1, 4>(mb, groups)
+                                     : gemm_fit_level<D, BITS, 1, 2>(mb, groups);
     }
 }
 
 template <int D>
-inline int gemm_fit_d(int bits, int nproj, int mb, int rows)
+inline int gemm_fit_d(int bits, int nproj, int mb, int rows, int groups)
 {
     switch (bits) {
-    case 8: return gemm_fit_db<D, 8>(nproj, mb, rows);
-    case 9: return gemm_fit_db<D, 9>(nproj, mb, rows);
-    case 10: return gemm_fit_db<D, 10>(nproj, mb, rows);
-    case 11: return gemm_fit_db<D, 11>(nproj, mb, rows);
-    case 12: return gemm_fit_db<D, 12>(nproj, mb, rows);
-    case 13: return gemm_fit_db<D, 13>(nproj, mb, rows);
+    case 8: return gemm_fit_db<D, 8>(nproj, mb, rows, groups);
+    case 9: return gemm_fit_db<D, 9>(nproj, mb, rows, groups);
+    case 10: return gemm_fit_db<D, 10>(nproj, mb, rows, groups);
+    case 11: return gemm_fit_db<D, 11>(nproj, mb, rows, groups);
+    case 12: return gemm_fit_db<D, 12>(nproj, mb, rows, groups);
+    case 13: return gemm_fit_db<D, 13>(nproj, mb, rows, groups);
     default: return 0;
     }
 }
 
-inline int gemm_fit(int d, int bits, int nproj, int mb, int rows)
+// rows, groups: the weight tensor's rows and 64-column groups per row
+inline int gemm_fit(int d, int bits, int nproj, int mb, int rows, int groups)
 {
-    return d == 2 ? gemm_fit_d<2>(bits, nproj, mb, rows)
-                  : (d == 4 ? gemm_fit_d<4>(bits, nproj, mb, rows) : gemm_fit_d<8>(bits, nproj, mb, rows));
+    return d == 2 ? gemm_fit_d<2>(bits, nproj, mb, rows, groups)
+                  : (d == 4 ? gemm_fit_d<4>(bits, nproj, mb, rows, groups)
+                            : gemm_fit_d<8>(bits, nproj, mb, rows, groups));
 }
 
-inline bool gemm_fits(int d, int bits, int nproj, int mb, int rows)
+inline bool gemm_fits(int d, int bits, int nproj, int mb, int rows, int groups)
 {
-    return gemm_fit(d, bits, nproj, mb, rows) > 0;
+    return gemm_fit(d, bits, nproj, mb, rows, groups) > 0;
 }
 
 template <int D>

@@ -691,6 +691,7 @@ def bench_stack(args, sw):
     achieved = float(kwork.mean() / k_mean / 1e9)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                # the record covers the 9-bit layers' kernel, not the mix timed here
                 "traffic": None,
                 "kernel": "vq::k_rows (gate+up+SwiGLU, fused), over the stack's layers",
                 "launch_us": round(k_mean * 1e6, 2), "bytes_per_launch": int(kwork.mean()),
@@ -808,7 +809,8 @@ def bench_fit(args, fw):
     achieved = encode_flops / k_mean / 1e12
     roofline = {"bound": "alu", "achieved": round(achieved, 2),
                 "peak": round(VALU_F32_OPS_PEAK_T, 1), "unit": "TFLOP/s",
-                "frac": round(achieved / VALU_F32_OPS_PEAK_T, 4), "traffic": None,
+                "frac": round(achieved / VALU_F32_OPS_PEAK_T, 4),
+                "traffic": recorded_traffic(args.workload, "fit"),
                 "kernel": "vq::k_fit_encode (nearest fp16 entry for every subvector, packed)",
                 "launch_us": round(k_mean * 1e6, 2), "flops_per_launch": int(encode_flops),
                 "timing": f"HIP event pair around each of {n_k} launches"}

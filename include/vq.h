@@ -176,8 +176,10 @@ vq_status vq_expert_gemm(const vq_tensor *W, int32_t n_x_rows, const void *x, vq
    three stages below, in order) run every batch of up to 16 tokens, and
    larger batches of at most 176 routed pairs (n_tokens*top_k) with hidden
    and inter at most 8192; other batches run the grouped MFMA GEMM
-   (vq_moe_ffn_engine says which).  workspace: device, at least vq_moe_ffn_workspace_size() bytes,
-   256-byte aligned. */
+   (vq_moe_ffn_engine says which); that path carries x, h and the down
+   projection's outputs in fp16 with power-of-two range scaling and
+   accumulates in fp32.  workspace: device, at least
+   vq_moe_ffn_workspace_size() bytes, 256-byte aligned. */
 size_t vq_moe_ffn_workspace_size(const vq_tensor *gate, const vq_tensor *up,
                                  const vq_tensor *down, int32_t n_tokens, int32_t top_k);
 vq_status vq_moe_ffn(const vq_tensor *gate, const vq_tensor *up, const vq_tensor *down,

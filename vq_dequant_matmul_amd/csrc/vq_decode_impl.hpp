@@ -590,6 +590,13 @@ __global__ __launch_bounds__(kThreads) void k_rows(const RowsArgs a)
     struct Unit {
         int item, e, row0;
     };
+    // The setup's own loads go first (the codebooks, and with one token the
+    // pairs' expert ids): loads return in issue order, so these arrive ahead
+    // of the first unit's rows instead of behind them.
+    CbRegs<D, BITS, NPROJ> cr;
+    load_codebooks<D, BITS, NPROJ>(a, cr);
+    const bool ids_held = one_token && P <= kThreads;
+    const int my_id = (ids_held && tid < P) ? load_global(a.ids + tid) : 0;
     // With one expert, or one token's pairs, a unit's expert is known without
     // the lists: its rows are requested before the setup below, so that the
     // memory latency overlaps the codebook staging.
@@ -611,10 +618,19 @@ __global__ __launch_bounds__(kThreads) void k_rows(const RowsArgs a)
     }
 
     // ---- setup: codebooks and work lists, once per workgroup -----------------
-    CbRegs<D, BITS, NPROJ> cr;
-    load_codebooks<D, BITS, NPROJ>(a, cr);
     const Lists L = lists_at(lds, a.list_offset, P);
-    if (one_token) {
+    if (ids_held) {
+        if (tid < P) {
+            L.ids[tid] = my_id;
+            L.uexp[tid] = my_id;
+            L.items[tid] = tid;
+            L.ustart[tid] = tid;
+        }
+        if (tid == 0) {
+            L.ustart[P] = P;
+            *L.U = P;
+        }
+    } else if (one_token) {
         single_token_lists(L, a.ids, P);
     } else if (a.ids) {
         for (int q = tid; q < P; q += kThreads)

@@ -503,6 +503,22 @@ __device__ __forceinline__ void single_token_lists(const Lists &L, const int32_t
     }
 }
 
+// The same with pair tid's expert id already in a register (P <= threads).
+__device__ __forceinline__ void single_token_lists_held(const Lists &L, int id, int P)
+{
+    const int q = threadIdx.x;
+    if (q < P) {
+        L.ids[q] = id;
+        L.uexp[q] = id;
+        L.items[q] = q;
+        L.ustart[q] = q;
+    }
+    if (q == 0) {
+        L.ustart[P] = P;
+        *L.U = P;
+    }
+}
+
 // Called by every thread after L.ids is filled and a barrier.
 __device__ __forceinline__ void build_lists(const Lists &L, int P)
 {
@@ -620,16 +636,7 @@ __global__ __launch_bounds__(kThreads) void k_rows(const RowsArgs a)
     // ---- setup: codebooks and work lists, once per workgroup -----------------
     const Lists L = lists_at(lds, a.list_offset, P);
     if (ids_held) {
-        if (tid < P) {
-            L.ids[tid] = my_id;
-            L.uexp[tid] = my_id;
-            L.items[tid] = tid;
-            L.ustart[tid] = tid;
-        }
-        if (tid == 0) {
-            L.ustart[P] = P;
-            *L.U = P;
-        }
+        single_token_lists_held(L, my_id, P);
     } else if (one_token) {
         single_token_lists(L, a.ids, P);
     } else if (a.ids) {
@@ -988,39 +995,92 @@ struct MixEngine {
     // found across those lanes, and each lane writes its four values as two
     // fp16 pairs.  Up to kHPasses passes of 16 (pair, group)s per workgroup
     // have their loads in flight together.
-    __device__ __forceinline__ void stage_h() const
+    static constexpr int kPerPass = kThreads / 16;
+    static constexpr int kHPasses = 8;
+    __device__ __forceinline__ int h_items() const { return P * a.groups; }
+    __device__ __forceinline__ void h_load(int base, float4 (&v)[kHPasses]) const
     {
-        constexpr int kPerPass = kThreads / 16;
-        constexpr int kHPasses = 8;
+        const int n = h_items();   // (pair, group) items; item i is h[64 i, 64 i + 64)
+        const int piece = tid & 15;
+#pragma unroll
+        for (int j = 0; j < kHPasses; ++j) {
+            const int it = min(base + j * kPerPass + (tid >> 4), n - 1);
+            const float4 *src = reinterpret_cast<const float4 *>(a.h) + (size_t)it * 16 + piece;
+            v[j] = *src;
+        }
+    }
+    __device__ __forceinline__ void h_store(int base, const float4 (&v)[kHPasses]) const
+    {
         uint32_t *xs = lds + a.x_offset;                           // [P][groups][kMixXStride]
         float *xm = reinterpret_cast<float *>(lds + a.m_offset);   // [P][groups]
-        const int n = P * a.groups;    // (pair, group) items; item i is h[64 i, 64 i + 64)
+        const int n = h_items();
         const int piece = tid & 15;
-        for (int base = 0; base < n; base += kPerPass * kHPasses) {
-            float4 v[kHPasses];
 #pragma unroll
-            for (int j = 0; j < kHPasses; ++j) {
-                const int it = min(base + j * kPerPass + (tid >> 4), n - 1);
-                const float4 *src = reinterpret_cast<const float4 *>(a.h) + (size_t)it * 16 + piece;
-                v[j] = *src;
-            }
-#pragma unroll
-            for (int j = 0; j < kHPasses; ++j) {
-                const int it = base + j * kPerPass + (tid >> 4);
-                const float m4 = fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)),
-                                       fmaxf(fabsf(v[j].z), fabsf(v[j].w)));
-                const int k = range_exponent(segment_max16_dpp(m4));
-                const float up = ldexpf(1.0f, k);
-                union { f16x2 h[2]; uint2 u; } o;
-                o.h[0] = pack_f16x2(v[j].x * up, v[j].y * up);
-                o.h[1] = pack_f16x2(v[j].z * up, v[j].w * up);
-                if (it < n) {
-                    *reinterpret_cast<uint2 *>(xs + (size_t)it * kMixXStride + 2 * piece) = o.u;
-                    if (piece == 0)
-                        xm[it] = ldexpf(1.0f, -k);
-                }
+        for (int j = 0; j < kHPasses; ++j) {
+            const int it = base + j * kPerPass + (tid >> 4);
+            const float m4 = fmaxf(fmaxf(fabsf(v[j].x), fabsf(v[j].y)),
+                                   fmaxf(fabsf(v[j].z), fabsf(v[j].w)));
+            const int k = range_exponent(segment_max16_dpp(m4));
+            const float up = ldexpf(1.0f, k);
+            union { f16x2 h[2]; uint2 u; } o;
+            o.h[0] = pack_f16x2(v[j].x * up, v[j].y * up);
+            o.h[1] = pack_f16x2(v[j].z * up, v[j].w * up);
+            if (it < n) {
+                *reinterpret_cast<uint2 *>(xs + (size_t)it * kMixXStride + 2 * piece) = o.u;
+                if (piece == 0)
+                    xm[it] = ldexpf(1.0f, -k);
             }
         }
+    }
+    __device__ __forceinline__ void stage_h(int from = 0) const
+    {
+        for (int base = from; base < h_items(); base += kPerPass * kHPasses) {
+            float4 v[kHPasses];
+            h_load(base, v);
+            h_store(base, v);
+        }
+    }
+
+    // One token: the setup's loads (the codebook in up to kEarlyCb 16-byte
+    // pieces a thread, the pairs' expert ids, the first pass of h) issued
+    // before the first item's rows, so they return ahead of them (loads
+    // return in issue order) and the setup is written while the rows are in
+    // flight.
+    static constexpr int kEarlyCb = 4;
+    struct Early {
+        uint4 cb[kEarlyCb];
+        int id;
+        float4 h[kHPasses];
+    };
+    __device__ __forceinline__ bool early_ok() const
+    {
+        return one && P <= kThreads && (a.cb_dwords & 3) == 0 &&
+               (a.cb_dwords >> 2) <= kEarlyCb * kThreads;
+    }
+    __device__ __forceinline__ void early_load(Early &x) const
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.codebook);
+        const int n4 = a.cb_dwords >> 2;
+#pragma unroll
+        for (int j = 0; j < kEarlyCb; ++j) {
+            const int i = tid + j * kThreads;
+            x.cb[j] = i < n4 ? src[i] : make_uint4(0u, 0u, 0u, 0u);
+        }
+        x.id = tid < P ? load_global(a.ids + tid) : 0;
+        h_load(0, x.h);
+    }
+    __device__ __forceinline__ void early_store(const Early &x) const
+    {
+        const int n4 = a.cb_dwords >> 2;
+#pragma unroll
+        for (int j = 0; j < kEarlyCb; ++j) {
+            const int i = tid + j * kThreads;
+            if (i < n4)
+                reinterpret_cast<uint4 *>(lds)[i] = x.cb[j];
+        }
+        single_token_lists_held(L, x.id, P);
+        h_store(0, x.h);
+        stage_h(kPerPass * kHPasses);
     }
 
     // After the stage_* calls: lists for several tokens and the waves' ranges.
@@ -1127,11 +1187,18 @@ __global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
     MixEngine<D, BITS> m(a, lds);
     typename MixEngine<D, BITS>::Chunk ca, cb;
     const bool pre = m.one && m.my_units > 0;
-    if (pre)
+    if (pre && m.early_ok()) {
+        typename MixEngine<D, BITS>::Early x;
+        m.early_load(x);
         m.load_item(ca, 0);
-    m.stage_codebook();
-    m.stage_lists();
-    m.stage_h();
+        m.early_store(x);
+    } else {
+        if (pre)
+            m.load_item(ca, 0);
+        m.stage_codebook();
+        m.stage_lists();
+        m.stage_h();
+    }
     m.finish_setup();
     m.run(ca, cb, pre);
 }

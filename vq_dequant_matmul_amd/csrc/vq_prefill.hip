@@ -442,8 +442,9 @@ static hipError_t launch_gemm(const TensorDev &t0, const TensorDev *t1, int mb, 
     a.out_e = out_e;
     if (out_e && (t1 || out_stride % 64 != 0 || out_stride != t0.rows))
         return hipErrorInvalidValue;
-    if (tile_cap > 0x7fffffff)
+    if (tile_cap > 0x7fffffff || tile_cap < 1)
         return hipErrorInvalidValue;
+    a.tile_cap = (int)tile_cap;
     switch (t0.d) {
     case 2: return gemm_d<2>(t0.bits, nproj, mb, a, (int)tile_cap, stream);
     case 4: return gemm_d<4>(t0.bits, nproj, mb, a, (int)tile_cap, stream);

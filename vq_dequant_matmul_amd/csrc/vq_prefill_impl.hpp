@@ -153,6 +153,7 @@ struct GemmArgs {
     const int32_t *perm;           // grouped position -> source index (NULL: identity)
     int act_div;                   // activation row = source index / act_div
     const int32_t *tiles;          // [n][3]: expert, first grouped position, rows
+    int tile_cap;                  // entries the tiles array holds
     const int32_t *n_tiles;
     int n_ntiles;                  // weight-row tiles per M tile
     const float *gate_in;          // split SwiGLU: gate outputs for this up projection
@@ -304,16 +305,24 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
     const int slot = L >> 3;
     const int tile = (slot / a.n_ntiles) * 8 + (L & 7);
     const int ntile = slot - (slot / a.n_ntiles) * a.n_ntiles;
-    if (tile >= *a.n_tiles)
+    // the tile's entry is read together with the tile count (one round trip
+    // instead of two): the grid's last workgroups may name tiles past the
+    // array, so the index is clamped to it and such a read is never used
+    const int tl = min(tile, a.tile_cap - 1);
+    const int e = a.tiles[3 * tl + 0];
+    const int m0 = a.tiles[3 * tl + 1];
+    const int mlen = a.tiles[3 * tl + 2];
+    const int n_tiles = *a.n_tiles;
+    // (the empty asm keeps the compiler from sinking the entry's loads below
+    // the early return, behind the tile count's round trip)
+    asm volatile("" : : "s"(e), "s"(m0), "s"(mlen), "s"(n_tiles));
+    if (tile >= n_tiles)
         return;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS bases in SGPRs
     const int h = lane >> 5;
-    const int e = a.tiles[3 * tile + 0];
-    const int m0 = a.tiles[3 * tile + 1];
-    const int mlen = a.tiles[3 * tile + 2];
     const int nblk = (mlen + 31) >> 5;
     // weight row of block nb of this lane: nrow0 + 32 * nb
     const int nrow0 = ntile * SH::WG_ROWS + wave * 32 * NN + (lane & 31);
@@ -340,29 +349,84 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
         for (int i = (n16 << 2) + tid; i < (a.cb_bytes[p] >> 2); i += NT)
             reinterpret_cast<uint32_t *>(dst)[i] = reinterpret_cast<const uint32_t *>(src)[i];
     }
-    float *kf = reinterpret_cast<float *>(smem + SH::KF_OFF);
-    for (int r = tid; r < 32 * MB; r += NT) {
-        const int p = m0 + min(r, mlen - 1);
-        const int row = a.perm ? a.perm[p] / a.act_div : p;
-        kf[r] = ldexpf(1.0f, -a.act_k[row]);
+    // ---- the prologue's global loads -------------------------------------------------------
+    // Every load below is issued before any of their results is used, and
+    // none sits in a branch of its own (a load in a branch, or one whose
+    // result the next branch tests, gets a wait right after it, and the
+    // round trips then run one after another).  The grouped-position map
+    // and the row maps are read through buffer resources based at the tile's
+    // first position and at the expert's first row; a missing map gets an
+    // empty resource, whose reads return 0 without an access, and a select
+    // takes the identity instead.
+    auto rsrc = [](const void *base, int bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes,
+                                                 0x00020000);
+    };
+    const bool has_perm = a.perm != nullptr;
+    const __amdgpu_buffer_rsrc_t r_perm =
+        rsrc(has_perm ? a.perm + m0 : nullptr, has_perm ? mlen * 4 : 0);
+    __amdgpu_buffer_rsrc_t r_map[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const bool hm = a.row_map[p] != nullptr;
+        r_map[p] = rsrc(hm ? a.row_map[p] + (int64_t)e * a.rows : nullptr, hm ? a.rows * 4 : 0);
     }
+    auto ld = [](const __amdgpu_buffer_rsrc_t &r, int i) {
+        return (int)__builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, 0);
+    };
+    // row factor of tile row tid (rows past the tile repeat its last row)
+    const int kr = min(tid, mlen - 1);
+    const int kperm = ld(r_perm, kr);
+    // this thread's activation-row loads
+    auto arow = [&](int q, int r) {
+        constexpr int TR = SH::TR, RPD = SH::RPD;
+        const int span = (TR - q * RPD < RPD) ? TR - q * RPD : RPD;
+        return q * RPD + (r - q * RPD) % span;
+    };
+    int aperm[SH::NDMA_A];
+#pragma unroll
+    for (int q = 0; q < SH::NDMA_A; ++q)
+        aperm[q] = ld(r_perm, min(arow(q, q * SH::RPD + (tid >> 3)), mlen - 1));
+    // weight rows of this lane's blocks (and, split SwiGLU, gate's map)
+    int rmap[NPB], gmap[NN];
+#pragma unroll
+    for (int p = 0; p < NPROJ; ++p)
+#pragma unroll
+        for (int nb = 0; nb < NN; ++nb)
+            rmap[p * NN + nb] = ld(r_map[p], min(nrow0 + 32 * nb, a.rows - 1));
+#pragma unroll
+    for (int nb = 0; nb < NN; ++nb)
+        gmap[nb] = NPROJ == 1 ? ld(r_map[1], min(nrow0 + 32 * nb, a.rows - 1)) : 0;
+    // rows of this lane's two-group chunk pieces
+    int cmap[SH::CHUNK ? NPB : 1][2];
+    if constexpr (SH::CHUNK) {
+#pragma unroll
+        for (int p = 0; p < NPROJ; ++p)
+#pragma unroll
+            for (int nb = 0; nb < NN; ++nb)
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+                    cmap[p * NN + nb][hh] = ld(
+                        r_map[p], min(ntile * SH::WG_ROWS + wave * 32 * NN + 32 * nb + 16 * hh +
+                                          (lane >> 2), a.rows - 1));
+    }
+    // the activation row's exponent (a second round trip when the rows are
+    // gathered through perm)
+    const int krow = has_perm ? kperm / a.act_div : m0 + kr;
+    const int kexp = a.act_k[krow];
+
+    float *kf = reinterpret_cast<float *>(smem + SH::KF_OFF);
     // activation rows: thread tid of load q fills tile row q*RPD + tid/8,
     // LDS chunk tid%8 with global chunk (tid%8) ^ (row%8).  Offsets fit 32
     // bits: the host keeps activation matrices below 4 GiB.
     // A load whose rows run past the tile (eight waves, three blocks) has
     // the waves past it repeat the rows of the first waves: the same bytes
     // to the same place, so every wave issues every load.
-    auto arow = [&](int q, int r) {
-        constexpr int TR = SH::TR, RPD = SH::RPD;
-        const int span = (TR - q * RPD < RPD) ? TR - q * RPD : RPD;
-        return q * RPD + (r - q * RPD) % span;
-    };
     uint32_t aoff[SH::NDMA_A];
 #pragma unroll
     for (int q = 0; q < SH::NDMA_A; ++q) {
         const int r = arow(q, q * SH::RPD + (tid >> 3));
-        const int p = m0 + min(r, mlen - 1);
-        const int row = a.perm ? a.perm[p] / a.act_div : p;
+        const int row = has_perm ? aperm[q] / a.act_div : m0 + min(r, mlen - 1);
         const int chunk = (tid & 7) ^ ((tid >> 3) & 7);
         aoff[q] = (uint32_t)row * (uint32_t)a.act_stride * 2u + (uint32_t)chunk * 16u;
     }
@@ -376,9 +440,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
         for (int nb = 0; nb < NN; ++nb) {
             const int n = nrow0 + 32 * nb;
             const int64_t lin = (int64_t)e * a.rows + min(n, a.rows - 1);
-            const int s = a.row_map[p] ? a.row_map[p][lin] : (int)lin;
+            const int s = a.row_map[p] ? rmap[p * NN + nb] : (int)lin;
             bool lv = (n < a.rows) && (s >= 0);
-            if (NPROJ == 1 && a.gate_in && a.row_map[1] && a.row_map[1][lin] < 0)
+            if (NPROJ == 1 && a.gate_in && a.row_map[1] && gmap[nb] < 0)
                 lv = false;   // split SwiGLU: a dead gate row gives h = +0.0
             const int pb = p * NN + nb;
             live |= lv ? (1 << pb) : 0;
@@ -412,7 +476,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
                 for (int hh = 0; hh < 2; ++hh) {
                     const int n = ntile * SH::WG_ROWS + wave * 32 * NN + 32 * nb + 16 * hh + r;
                     const int64_t lin = (int64_t)e * a.rows + min(n, a.rows - 1);
-                    const int sr = a.row_map[p] ? a.row_map[p][lin] : (int)lin;
+                    const int sr = a.row_map[p] ? cmap[p * NN + nb][hh] : (int)lin;
                     // a dead or missing row reads row 0: its outputs are zeroed
                     cptr[p * NN + nb][hh] = a.codes[p] + (int64_t)max(sr, 0) * a.wpr + piece * 4;
                 }
@@ -434,6 +498,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm(const GemmArgs a)
         ssel[pb] = !lv ? 0x0c0c0c0cu : (hi ? 0x03020302u : 0x01000100u);
         sflip[pb] = lv ? 0x02020202u : 0u;   // 0x01000100 <-> 0x03020302
     }
+
+    static_assert(NT >= 32 * MB, "one row factor per thread");
+    if (tid < 32 * MB)
+        kf[tid] = ldexpf(1.0f, -kexp);
 
     // ---- the loads of one step g, one instruction per unit: per (projection,
     // block) a scale load and the code window of group gc into code stage cst

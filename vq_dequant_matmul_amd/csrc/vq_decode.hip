@@ -187,6 +187,10 @@ hipError_t launch_rows(const RowsLaunch &L, hipStream_t stream)
     // with their hi + lo terms, stay faster at two passes.)
     if (L.act_f32 == 0 && (int64_t)P * a.tiles < (int64_t)kRowsOnePassUnitsPerCu * n_cu)
         lds = (size_t)rows_args(L, a, gpl, 1) * 4;
+    // one projection with many units (the down stage of a few tokens): four
+    // row passes per unit, so a unit's fixed work covers twice the rows
+    else if (L.nproj == 1 && (int64_t)P * a.tiles >= (int64_t)kRowsFourPassUnitsPerCu * n_cu)
+        lds = (size_t)rows_args(L, a, gpl, 4) * 4;
     // a projection whose rows are all dead (skip-zero) stores nothing: every
     // output row it touches is exactly zero (for SwiGLU, silu(0)*u = 0 and
     // silu(g)*0 = 0 are written as +0.0)

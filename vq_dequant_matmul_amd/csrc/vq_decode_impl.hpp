@@ -41,6 +41,7 @@ constexpr int kThreads = 64 * kWaves;
 // a launch with bf16 activations and fewer units than this many per CU at
 // two row passes per unit takes one pass per unit
 constexpr int kRowsOnePassUnitsPerCu = 6;
+constexpr int kRowsFourPassUnitsPerCu = 16;
 
 struct RowsArgs {
     const uint32_t *codes[2];
@@ -1284,6 +1285,10 @@ static hipError_t rows_act(const RowsArgs &a, int act, int64_t units, int n_cu, 
 {
     if (a.iters == 1)
         return rows_iters<D, BITS, GPL, NPROJ, 1>(a, act, units, n_cu, lds, s);
+    if constexpr (NPROJ == 1) {
+        if (a.iters == 4)
+            return rows_iters<D, BITS, GPL, NPROJ, 4>(a, act, units, n_cu, lds, s);
+    }
     return rows_iters<D, BITS, GPL, NPROJ, 2>(a, act, units, n_cu, lds, s);
 }
 

@@ -38,6 +38,7 @@ GEMM_CASES = [
     # 8-bit d2 blocks near 100 rows: 128-row tiles in the chunk-only LDS layout
     (2, 8, 600, 512, 4, [100, 128, 97, 33], "bf16", 11),
     (2, 8, 1024, 1024, 3, [120, 88, 101], "bf16", 0),
+    (2, 8, 700, 768, 4, [128, 120, 7, 110], "bf16", 21),   # one-block tile among 128-row ones
     # the same block sizes with 7 groups a row: no chunks, 96-row tiles
     (2, 8, 300, 448, 4, [100, 128, 97, 33], "bf16", 0),
 ]

@@ -845,7 +845,6 @@ struct MixArgs {
 };
 
 constexpr int kMixXStride = 36;   // dwords per (pair, group): 32 used, padded for ds_read_b128
-constexpr int kMixChunk = 4;      // experts whose rows are loaded together
 
 // The engine of k_mix, in the pieces a caller runs in order: load_item(first)
 // (optional, before the setup), the setup (stage_codebook, stage_lists,
@@ -853,13 +852,16 @@ constexpr int kMixChunk = 4;      // experts whose rows are loaded together
 //
 // A workgroup walks tiles of rpw output rows (blockIdx.x, + gridDim.x,
 // ...); its waves split the distinct experts into contiguous ranges of at
-// most per = ceil(U / waves), taken kMixChunk at a time.  Work item i of a
+// most per = ceil(U / waves), taken CH (2 or 4) at a time: the launch picks
+// the smaller when no wave has more than two experts, so no load slot of a
+// batch is spent on a repeated expert.  Work item i of a
 // wave is (tile i / nch, chunk i % nch); the words of item i+1 are in flight
 // while item i is computed.  For a single token the experts are the ids
 // themselves, so the first item can be requested before the setup and its
 // memory latency overlaps it.
-template <int D, int BITS>
+template <int D, int BITS, int CH>
 struct MixEngine {
+    static constexpr int kMixChunk = CH;   // experts whose rows are loaded together
     using GM = Geom<D, BITS>;
     static constexpr int NW = GM::NW;
     static constexpr int G = GM::G;
@@ -1181,15 +1183,15 @@ struct MixEngine {
     }
 };
 
-template <int D, int BITS>
+template <int D, int BITS, int CH>
 __global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-    MixEngine<D, BITS> m(a, lds);
-    typename MixEngine<D, BITS>::Chunk ca, cb;
+    MixEngine<D, BITS, CH> m(a, lds);
+    typename MixEngine<D, BITS, CH>::Chunk ca, cb;
     const bool pre = m.one && m.my_units > 0;
     if (pre && m.early_ok()) {
-        typename MixEngine<D, BITS>::Early x;
+        typename MixEngine<D, BITS, CH>::Early x;
         m.early_load(x);
         m.load_item(ca, 0);
         m.early_store(x);
@@ -1204,10 +1206,10 @@ __global__ __launch_bounds__(kThreads) void k_mix(const MixArgs a)
     m.run(ca, cb, pre);
 }
 
-template <int D, int BITS>
-static hipError_t mix_db(const MixArgs &a, size_t lds, hipStream_t stream)
+template <int D, int BITS, int CH>
+static hipError_t mix_dbc(const MixArgs &a, size_t lds, hipStream_t stream)
 {
-    auto kern = k_mix<D, BITS>;
+    auto kern = k_mix<D, BITS, CH>;
     if (lds > 65536) {
         hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1218,6 +1220,17 @@ static hipError_t mix_db(const MixArgs &a, size_t lds, hipStream_t stream)
     const int wgs = a.units < a.max_wgs ? a.units : a.max_wgs;
     hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kThreads), lds, stream, a);
     return hipGetLastError();
+}
+
+// Experts per load batch: two when one token's pairs leave every wave at
+// most two experts, else four.
+template <int D, int BITS>
+static hipError_t mix_db(const MixArgs &a, size_t lds, hipStream_t stream)
+{
+    const int P = a.n_tok * a.top_k;
+    if (a.n_tok == 1 && (P + kWaves - 1) / kWaves <= 2)
+        return mix_dbc<D, BITS, 2>(a, lds, stream);
+    return mix_dbc<D, BITS, 4>(a, lds, stream);
 }
 
 template <int D>

@@ -174,7 +174,8 @@ vq_status vq_expert_gemm(const vq_tensor *W, int32_t n_x_rows, const void *x, vq
    x_dtype; topk_ids int32 and topk_weights fp32 [n_tokens][top_k];
    y: [n_tokens][hidden] fp32.  The bandwidth-bound decode kernels (the
    three stages below, in order) run every batch of up to 16 tokens, and
-   larger batches of at most 176 routed pairs (n_tokens*top_k) with hidden
+   larger batches of at most max(176, 3*n_experts/4) routed pairs
+   (n_tokens*top_k) with hidden
    and inter at most 8192; other batches run the grouped MFMA GEMM
    (vq_moe_ffn_engine says which); that path carries x, h and the down
    projection's outputs in fp16 with power-of-two range scaling and

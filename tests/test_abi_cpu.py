@@ -206,8 +206,8 @@ def test_noalloc_refuses_batches_beyond_its_array(lib):
 
 def test_ffn_engine_choice(lib):
     """vq_moe_ffn_engine (host only): the decode kernels for up to 16 tokens,
-    and past that for at most 176 routed pairs with hidden and inter at most
-    8192; the grouped GEMM otherwise."""
+    and past that for at most max(176, 3/4 of the experts) routed pairs with
+    hidden and inter at most 8192; the grouped GEMM otherwise."""
     def engine(T, k, E, H=4096, I=1024):
         g = _t(rows=I, cols=H, n_experts=E, n_stored=E * I)
         u = _t(rows=I, cols=H, n_experts=E, n_stored=E * I)
@@ -221,7 +221,9 @@ def test_ffn_engine_choice(lib):
     assert engine(0, 8, 128) == D and engine(1, 10, 512) == D and engine(16, 10, 512) == D
     assert engine(16, 64, 64, H=1024, I=512) == D    # 1024 pairs: by token count
     assert engine(17, 10, 512) == D       # 170 pairs
-    assert engine(18, 10, 512) == M       # 180 pairs
+    assert engine(38, 10, 512) == D       # 380 pairs (limit 384 at 512 experts)
+    assert engine(39, 10, 512) == M       # 390 pairs
+    assert engine(18, 10, 200) == M       # 180 pairs: 176 at 200 experts
     assert engine(22, 8, 128) == D        # 176 pairs
     assert engine(23, 8, 128) == M
     assert engine(17, 8, 128, H=16384) == M   # hidden past the decode kernels

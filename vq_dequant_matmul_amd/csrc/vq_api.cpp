@@ -127,17 +127,26 @@ constexpr int kDecodeMaxTokens = 16;
 constexpr int kGemvMaxTokens = 64;
 
 // Past kDecodeMaxTokens tokens the routed FFN stays on the decode kernels
-// while the batch has at most this many routed pairs.  The decode kernels
-// cost about the same per pair at any batch size (every pair streams its
-// expert's rows), while the grouped GEMM reads an expert once per tile of
-// its pairs but pays a fixed cost per call (routing, row scaling, the
-// combine, tiles of 64 rows that small batches leave mostly empty).  On the
-// 512-expert top-10 layer (6.3 MB per routed expert) the two cost the same
-// near 190 pairs, on the 128-expert top-8 one (1.3 MB) near 165.
+// while the batch has at most max(kDecodeMaxPairs, 3/4 of the experts)
+// routed pairs.  The decode kernels cost about the same per pair at any
+// batch size (every pair streams its expert's rows), while the grouped GEMM
+// reads an expert once per tile of its pairs but pays a fixed cost per call
+// (routing, row scaling, the combine, tiles that small batches leave mostly
+// empty); its cost grows with the distinct experts a batch touches, so the
+// crossover moves out with the expert count.  Measured: on the 512-expert
+// top-10 layer (6.3 MB per routed expert) decode 0.56 ms against 0.60 at
+// 320 pairs, 1.10 against 0.86 at 640 (the two meet near 380); on the
+// 128-expert top-8 one (1.3 MB) near 240, decode 0.187 ms against 0.179 at
+// 256 pairs.
 #ifndef VQ_DECODE_MAX_PAIRS
 #define VQ_DECODE_MAX_PAIRS 176
 #endif
 constexpr int kDecodeMaxPairs = VQ_DECODE_MAX_PAIRS;
+
+static int64_t decode_pair_limit(const vq_tensor &gate)
+{
+    return std::max<int64_t>(kDecodeMaxPairs, (int64_t)gate.n_experts * 3 / 4);
+}
 
 }  // namespace
 
@@ -536,7 +545,7 @@ static vq_status check_ffn(const vq_tensor *gate, const vq_tensor *up, const vq_
 
 // Which engine runs the routed FFN (arguments already checked): the decode
 // kernels for up to kDecodeMaxTokens tokens (whose size limits then apply),
-// and for larger batches of at most kDecodeMaxPairs routed pairs whose
+// and for larger batches of at most decode_pair_limit() routed pairs whose
 // columns fit the decode kernels; otherwise the grouped MFMA GEMM.
 static bool ffn_uses_decode(const vq_tensor &gate, const vq_tensor &down, int32_t n_tokens,
                             int32_t top_k)
@@ -544,7 +553,7 @@ static bool ffn_uses_decode(const vq_tensor &gate, const vq_tensor &down, int32_
     if (n_tokens <= kDecodeMaxTokens)
         return true;
     const int64_t pairs = (int64_t)n_tokens * top_k;
-    return pairs <= kDecodeMaxPairs && pairs <= vq::kMaxSlots &&
+    return pairs <= decode_pair_limit(gate) && pairs <= vq::kMaxSlots &&
            gate.cols / 64 <= vq::kMaxGroupsDecode && down.cols / 64 <= vq::kMaxGroupsDecode;
 }
 

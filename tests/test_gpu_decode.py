@@ -209,14 +209,17 @@ def test_moe_batch_full_size(name, engine):
     check_close(y, oracle.moe_ffn(gate, up, down, x, ids, w), name)
 
 
-@pytest.mark.parametrize("T,engine", [
-    (44, vq.VQ_ENGINE_DECODE),    # 176 routed pairs
-    (45, vq.VQ_ENGINE_MFMA),      # 180
+@pytest.mark.parametrize("E,T,engine", [
+    (32, 44, vq.VQ_ENGINE_DECODE),     # 176 routed pairs
+    (32, 45, vq.VQ_ENGINE_MFMA),       # 180
+    (512, 96, vq.VQ_ENGINE_DECODE),    # 384 = 3/4 of the experts
+    (512, 97, vq.VQ_ENGINE_MFMA),      # 388
 ])
-def test_moe_batch_engine_boundary(T, engine):
-    """Either side of the engine switch: same layer, both engines, both
-    against the oracle."""
-    E, k, H, I = 32, 4, 256, 128
+def test_moe_batch_engine_boundary(E, T, engine):
+    """Either side of the engine switch, at the fixed 176-pair limit and at
+    the expert-count limit: same layer, both engines, both against the
+    oracle."""
+    k, H, I = 4, 256, 128
     wl = synth.MoEWorkload("boundary", E, k, H, I, 4, 9, T, seed=95)
     gate = synth.make_tensor(wl.seed, 1, rows=I, cols=H, d=4, bits=9, n_experts=E, dead_rows=2)
     up = synth.make_tensor(wl.seed, 2, rows=I, cols=H, d=4, bits=9, n_experts=E)
